@@ -1,0 +1,314 @@
+"""CPU oracle for SPADE's executor hot path (test infrastructure only).
+
+This module is the plain, slow, obviously-correct statement of what the
+block-sparse attention path computes.  Only the tests, the graft smoke check
+and the bench's CPU-baseline leg may import it; the product library never
+does, and the two share no code.
+
+Source: "SPADE: An Input-Adaptive Sparse Attention Engine for Fast Video
+Diffusion Models Inference", the gist.science technical summary of the paper
+(page https://gist.science/paper/2608.03335), sections "Problem Statement",
+"Methodology 1. vDiT-SSR" (Blocking Scheme Candidates; Summarizer & Estimator
+Expressions) and "Methodology 3. Head-wise Sparse Attention Execution" (Flash
+Block-Sparse Attention), plus the abstract on the catalyzex author pages
+(executor with index search and flash block-sparse attention).
+
+Arithmetic is fp64 unless a step states otherwise.  Readings taken where the
+pages are silent (each also listed in the design notes):
+
+* tokens are flattened in raster order n = (t*Hh + h)*W + w;
+* blocks tile the grid from the origin with stride (bt, bh, bw); the last
+  block along an axis that the block size does not divide is partial; block
+  j = (it*nH + ih)*nW + iw; Q and KV use the same tiling;
+* the Summarizer is the mean over the block's real tokens, computed exactly
+  and stored as fp32 (the summary tensor's storage type);
+* the inter-block Estimator is S_ij = scale * <qbar_i, kbar_j>, scale = 1/sqrt(d);
+* selection orders blocks by (S descending, j ascending); a count or ratio
+  budget keeps the first k (k = ceil(r*nK - 1e-6) clamped to [1, nK] for a
+  ratio); a mass budget keeps the shortest prefix whose softmax(S) mass over
+  all nK blocks reaches tau (at least one block);
+* attention is exact softmax attention of each query over all tokens of its
+  kept KV blocks, renormalised over those keys only; every Q block is
+  computed; output keeps the input raster layout.
+
+Parity pins: blocking, summaries, estimate, selection and attention are each
+pinned against closed forms, brute force and library routines in
+tests/test_oracle_pins.py.  Parity against the authors' implementation itself
+is unpinned (the pages print no code, equation or worked example).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+MODE_COUNT = "count"
+MODE_RATIO = "ratio"
+MODE_MASS = "mass"
+
+
+# ---------------------------------------------------------------------------
+# 3D blocking of the latent token grid (vDiT-SSR, Blocking Scheme Candidates)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Geometry:
+    T: int
+    Hh: int
+    W: int
+    bt: int
+    bh: int
+    bw: int
+
+    @property
+    def N(self) -> int:
+        return self.T * self.Hh * self.W
+
+    @property
+    def counts(self) -> Tuple[int, int, int]:
+        return (-(-self.T // self.bt), -(-self.Hh // self.bh), -(-self.W // self.bw))
+
+    @property
+    def nblk(self) -> int:
+        a, b, c = self.counts
+        return a * b * c
+
+
+def block_extents(g: Geometry) -> List[Tuple[int, int, int, int, int, int]]:
+    """Per block j: (t0, t1, h0, h1, w0, w1), half-open, in block order."""
+    nT, nH, nW = g.counts
+    out = []
+    for it in range(nT):
+        for ih in range(nH):
+            for iw in range(nW):
+                out.append((it * g.bt, min(g.T, (it + 1) * g.bt),
+                            ih * g.bh, min(g.Hh, (ih + 1) * g.bh),
+                            iw * g.bw, min(g.W, (iw + 1) * g.bw)))
+    return out
+
+
+def block_tokens(g: Geometry) -> List[np.ndarray]:
+    """Raster token ids of each block, listed t-major, then h, then w."""
+    toks = []
+    for (t0, t1, h0, h1, w0, w1) in block_extents(g):
+        t = np.arange(t0, t1)[:, None, None]
+        h = np.arange(h0, h1)[None, :, None]
+        w = np.arange(w0, w1)[None, None, :]
+        toks.append(((t * g.Hh + h) * g.W + w).reshape(-1))
+    return toks
+
+
+def token_block_ids(g: Geometry) -> np.ndarray:
+    """[N] block id of every token (brute force over the block list)."""
+    ids = np.full(g.N, -1, dtype=np.int64)
+    for j, tk in enumerate(block_tokens(g)):
+        ids[tk] = j
+    return ids
+
+
+# ---------------------------------------------------------------------------
+# Summarizer (vDiT-SSR, Summarizer & Estimator Expressions): block mean
+# ---------------------------------------------------------------------------
+
+def summarize(x: np.ndarray, g: Geometry, store_f32: bool = True) -> np.ndarray:
+    """Block means of x [B, H, N, d] -> [B, H, nblk, d].
+
+    The sum over the block's real tokens is taken in fp64 and divided once by
+    the token count; with store_f32 the mean is rounded to fp32 (returned as
+    fp64 holding fp32 values).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, H, N, d = x.shape
+    assert N == g.N
+    toks = block_tokens(g)
+    out = np.empty((B, H, len(toks), d), dtype=np.float64)
+    for j, tk in enumerate(toks):
+        out[:, :, j, :] = x[:, :, tk, :].sum(axis=2) / float(len(tk))
+    if store_f32:
+        out = out.astype(np.float32).astype(np.float64)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Estimator (inter-block importance scores)
+# ---------------------------------------------------------------------------
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def estimate(qm: np.ndarray, km: np.ndarray, scale: float) -> np.ndarray:
+    """S[b, h, i, j] = scale * <qbar_i, kbar_j> in fp64."""
+    return scale * np.matmul(qm, np.swapaxes(km, -1, -2))
+
+
+# ---------------------------------------------------------------------------
+# Index search: which KV blocks each Q block keeps
+# ---------------------------------------------------------------------------
+
+def keep_count(mode: str, value: float, nK: int) -> int:
+    """Blocks kept per row for a count or ratio budget."""
+    if mode == MODE_COUNT:
+        k = int(value)
+        if k != value or k < 1 or k > nK:
+            raise ValueError("count budget must be an integer in [1, nK]")
+        return k
+    if mode == MODE_RATIO:
+        r = float(np.float32(value))
+        if not (0.0 < r <= 1.0):
+            raise ValueError("ratio budget must be in (0, 1]")
+        return min(nK, max(1, math.ceil(r * nK - 1e-6)))
+    raise ValueError(mode)
+
+
+@dataclass
+class Selection:
+    row_ptr: np.ndarray  # [R + 1] int64
+    col_idx: np.ndarray  # [nnz] int64, ascending within each row
+    counts: np.ndarray  # [R]
+    margins: np.ndarray  # [R] decision margin of each row (inf if forced)
+    order: np.ndarray  # [R, nK] the (S desc, j asc) order of each row
+
+    def row(self, r: int) -> np.ndarray:
+        return self.col_idx[self.row_ptr[r]:self.row_ptr[r + 1]]
+
+
+def select(S: np.ndarray, mode: str, per_head: Sequence[float]) -> Selection:
+    """Select KV blocks per row of S [B, H, nQ, nK]; rows r = (b*H + h)*nQ + i."""
+    B, H, nQ, nK = S.shape
+    per_head = [float(np.float32(v)) for v in per_head]
+    assert len(per_head) == H
+    S2 = S.reshape(B * H * nQ, nK)
+    R = S2.shape[0]
+    head_of_row = (np.arange(R) // nQ) % H
+    # descending S with ties broken by ascending j (stable sort of -S)
+    order = np.argsort(-S2, axis=1, kind="stable")
+    s_sorted = np.take_along_axis(S2, order, axis=1)
+    counts = np.empty(R, dtype=np.int64)
+    margins = np.empty(R, dtype=np.float64)
+    if mode in (MODE_COUNT, MODE_RATIO):
+        for r in range(R):
+            k = keep_count(mode, per_head[head_of_row[r]], nK)
+            counts[r] = k
+            margins[r] = (s_sorted[r, k - 1] - s_sorted[r, k]) if k < nK else math.inf
+    elif mode == MODE_MASS:
+        for r in range(R):
+            tau = per_head[head_of_row[r]]
+            if not (0.0 < tau <= 1.0):
+                raise ValueError("mass budget must be in (0, 1]")
+            # softmax of the row over all nK blocks, taken in descending order
+            p = np.exp(s_sorted[r] - s_sorted[r, 0])
+            Z = p.sum()
+            csum = np.cumsum(p)
+            hit = np.nonzero(csum >= tau * Z)[0]
+            k = int(hit[0]) + 1 if hit.size else nK
+            counts[r] = k
+            c_k = csum[k - 1] / Z
+            c_prev = csum[k - 2] / Z if k >= 2 else 0.0
+            m = tau - c_prev
+            if k < nK:
+                m = min(m, s_sorted[r, k - 1] - s_sorted[r, k], c_k - tau)
+            margins[r] = m
+    else:
+        raise ValueError(mode)
+    row_ptr = np.zeros(R + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col_idx = np.empty(int(row_ptr[-1]), dtype=np.int64)
+    for r in range(R):
+        col_idx[row_ptr[r]:row_ptr[r + 1]] = np.sort(order[r, :counts[r]])
+    return Selection(row_ptr, col_idx, counts, margins, order)
+
+
+# ---------------------------------------------------------------------------
+# Attention over the kept blocks (exact softmax; online softmax reaches the
+# same values, only faster)
+# ---------------------------------------------------------------------------
+
+def attention_block_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, toks: List[np.ndarray],
+                        i: int, kept: Iterable[int], scale: float,
+                        return_weights: bool = False):
+    """Output rows of Q block i for one (b, h).
+
+    q, k, v are [N, d] fp64 of that head; kept lists KV blocks.
+    Returns o [n_i, d] (and the [n_i, n_keys] weights and key ids if asked).
+    """
+    kept = list(kept)
+    qi = q[toks[i]]
+    key_ids = np.concatenate([toks[j] for j in kept])
+    logits = scale * (qi @ k[key_ids].T)
+    logits = logits - logits.max(axis=1, keepdims=True)
+    w = np.exp(logits)
+    w = w / w.sum(axis=1, keepdims=True)
+    o = w @ v[key_ids]
+    if return_weights:
+        return o, w, key_ids
+    return o
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: Geometry,
+              row_ptr: np.ndarray, col_idx: np.ndarray, scale: float,
+              rows: Optional[Iterable[int]] = None) -> Dict[int, np.ndarray]:
+    """Block-sparse attention of the given rows (default all) for any CSR.
+
+    q, k, v: [B, H, N, d] (converted to fp64).  Returns {row: o [n_i, d]}.
+    """
+    B, H, N, d = q.shape
+    nblk = g.nblk
+    toks = block_tokens(g)
+    R = B * H * nblk
+    rows = range(R) if rows is None else rows
+    out = {}
+    cache = {}
+    for r in rows:
+        bh, i = divmod(int(r), nblk)
+        b, h = divmod(bh, H)
+        if bh not in cache:
+            cache.clear()
+            cache[bh] = tuple(np.asarray(t[b, h], dtype=np.float64) for t in (q, k, v))
+        qh, kh, vh = cache[bh]
+        kept = [int(j) for j in col_idx[row_ptr[r]:row_ptr[r + 1]]]
+        out[int(r)] = attention_block_row(qh, kh, vh, toks, i, kept, scale)
+    return out
+
+
+def attention_full(q, k, v, g: Geometry, row_ptr, col_idx, scale) -> np.ndarray:
+    """Whole output [B, H, N, d] in the input raster layout."""
+    B, H, N, d = q.shape
+    toks = block_tokens(g)
+    O = np.zeros((B, H, N, d), dtype=np.float64)
+    for r, o in attention(q, k, v, g, row_ptr, col_idx, scale).items():
+        bh, i = divmod(r, g.nblk)
+        b, h = divmod(bh, H)
+        O[b, h, toks[i]] = o
+    return O
+
+
+def dense_attention(q, k, v, scale: float) -> np.ndarray:
+    """Full softmax attention softmax(scale*Q K^T) V per (b, h), fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    logits = scale * np.matmul(q, np.swapaxes(k, -1, -2))
+    logits -= logits.max(axis=-1, keepdims=True)
+    w = np.exp(logits)
+    w /= w.sum(axis=-1, keepdims=True)
+    return np.matmul(w, v)
+
+
+# ---------------------------------------------------------------------------
+# whole path
+# ---------------------------------------------------------------------------
+
+def spade_attn(q, k, v, g: Geometry, mode: str, per_head: Sequence[float],
+               scale: Optional[float] = None):
+    """Summaries -> scores -> selection -> attention.  Returns (O, Selection, S)."""
+    d = q.shape[-1]
+    scale = default_scale(d) if scale is None else float(scale)
+    qm = summarize(q, g)
+    km = summarize(k, g)
+    S = estimate(qm, km, scale)
+    sel = select(S, mode, per_head)
+    O = attention_full(q, k, v, g, sel.row_ptr, sel.col_idx, scale)
+    return O, sel, S
