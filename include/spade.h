@@ -1,0 +1,148 @@
+/*
+ * spade.h -- C ABI of the MI355X (gfx950) block-sparse video attention library.
+ *
+ * The library runs the hot path of SPADE's executor ("SPADE: An Input-Adaptive
+ * Sparse Attention Engine for Fast Video Diffusion Models Inference"; the
+ * gist.science technical summary, "Methodology 1. vDiT-SSR" and
+ * "3. Head-wise Sparse Attention Execution"): per attention head it
+ *   1. summarizes every 3D (t, h, w) block of Q and K by its mean,
+ *   2. estimates block-to-block scores S = scale * qbar kbar^T,
+ *   3. selects, for each Q block, the KV blocks to keep (index search) and
+ *      emits them as a block-sparse row list (CSR), and
+ *   4. runs flash-style block-sparse attention over only the kept blocks.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors Q, K, V, O are contiguous [B, H, N, d] with d innermost and the
+ *   N = T*Hh*W tokens in raster order n = (t*Hh + h)*W + w.
+ * - Blocks tile the grid from the origin with stride (bt, bh, bw); the last
+ *   block along an axis that the block size does not divide is partial.
+ *   nT = ceil(T/bt), nH = ceil(Hh/bh), nW = ceil(W/bw), nblk = nT*nH*nW and
+ *   block j = (it*nH + ih)*nW + iw.  Q and KV blocks use the same tiling.
+ * - Selection rows: r = (b*H + h)*nblk + i, R = B*H*nblk rows.
+ *   row_ptr[R+1] (int32) and col_idx[nnz] (int32) form a CSR whose row r lists
+ *   the kept KV block ids of Q block i of head (b, h) in ascending order.
+ * - Pointers named q, k, v, o, q_mean, k_mean, row_ptr, col_idx, scores and
+ *   workspace are DEVICE pointers owned by the caller.  spade_problem and
+ *   spade_budget (and budget->per_head) are HOST memory read during the call.
+ *   The library never allocates or frees device memory and keeps no state
+ *   other than a per-device cache of the compute-unit count.
+ * - Every compute call validates its arguments on the host first; on any
+ *   error it returns a status and launches nothing.  Launches are
+ *   asynchronous on `stream` (a hipStream_t; NULL = the default stream); the
+ *   library never synchronizes the device.  A failed launch returns
+ *   SPADE_ERR_DEVICE.
+ * - NaN or Inf inputs give unspecified (but memory-safe) results.
+ * - Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef SPADE_H
+#define SPADE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spade_status {
+  SPADE_OK = 0,
+  SPADE_ERR_INVALID_ARG = 1, /* null pointer, inconsistent shape, bad budget */
+  SPADE_ERR_UNSUPPORTED = 2, /* valid but outside the supported set */
+  SPADE_ERR_CAPACITY = 3,    /* col_idx or workspace too small */
+  SPADE_ERR_DEVICE = 4       /* a HIP runtime call or launch failed */
+} spade_status;
+
+typedef enum spade_dtype {
+  SPADE_BF16 = 0, /* Q/K/V/O bf16; attention on bf16 MFMA, fp32 softmax */
+  SPADE_F32 = 1   /* Q/K/V/O fp32; attention in fp32 FMA (debug mode) */
+} spade_dtype;
+
+typedef enum spade_keep_mode {
+  SPADE_KEEP_COUNT = 0, /* keep k_h blocks per row, k_h integral in [1, nblk] */
+  SPADE_KEEP_RATIO = 1, /* keep k_h = clamp(ceil(r_h*nblk - 1e-6), 1, nblk), r_h in (0, 1] */
+  SPADE_KEEP_MASS = 2   /* keep the shortest score-ordered prefix whose softmax(S)
+                           mass over all nblk blocks reaches tau_h, tau_h in (0, 1] */
+} spade_keep_mode;
+
+/* Shape of one attention layer.
+ * Supported: d in {64, 128}; B*H >= 0; 1 <= nblk <= 4096; N == T*Hh*W;
+ * bt*bh*bw <= 1024; B*H*nblk < 2^31 rows.  scale == 0 selects 1/sqrt(d). */
+typedef struct spade_problem {
+  int32_t B, H, N, d;
+  int32_t T, Hh, W;
+  int32_t bt, bh, bw;
+  int32_t dtype; /* spade_dtype */
+  float scale;
+} spade_problem;
+
+/* Per-head keep budget: per_head is a HOST array of H values interpreted by
+ * mode.  The same budget applies to every batch entry. */
+typedef struct spade_budget {
+  int32_t mode; /* spade_keep_mode */
+  const float* per_head;
+} spade_budget;
+
+/* ---- host-only helpers (no device access) ------------------------------ */
+
+/* nblk of the problem, or -1 if the shape is invalid. */
+int32_t spade_num_blocks(const spade_problem* p);
+
+/* Entries col_idx must hold: exact for COUNT/RATIO, the worst case R*nblk
+ * for MASS.  -1 if the problem or budget is invalid. */
+int64_t spade_max_nnz(const spade_problem* p, const spade_budget* budget);
+
+/* Bytes of device workspace that every compute entry point of this problem
+ * needs (the maximum over them); 0 if the problem is invalid. */
+size_t spade_workspace_bytes(const spade_problem* p);
+
+/* Full host-side validation of a problem, a budget (may be NULL) and a
+ * col_idx capacity in entries (pass -1 to skip the capacity check). */
+spade_status spade_check(const spade_problem* p, const spade_budget* budget, int64_t col_capacity);
+
+/* Static string naming a status. */
+const char* spade_status_string(spade_status s);
+
+/* ---- compute entry points ----------------------------------------------- */
+
+/* Summarizer ("Summarizer & Estimator Expressions"; fused blocking and
+ * summarization of "Kernel Fusion"): q_mean[b,h,j,:] = mean of q over the real
+ * tokens of block j (likewise k).  Sums are exact (fp64) and the mean is
+ * rounded once to fp32.  q_mean, k_mean: fp32 [B, H, nblk, d]. */
+spade_status spade_summarize(const spade_problem* p, const void* q, const void* k,
+                             float* q_mean, float* k_mean, void* stream);
+
+/* Estimator + index search: S_ij = scale * <q_mean_i, k_mean_j> in fp64, then
+ * per row the blocks in (S descending, j ascending) order are kept by the
+ * budget.  Writes row_ptr [R+1] and col_idx (ascending ids per row).
+ * col_capacity (entries) must be >= spade_max_nnz.  Workspace as given by
+ * spade_workspace_bytes. */
+spade_status spade_estimate_select(const spade_problem* p, const float* q_mean, const float* k_mean,
+                                   const spade_budget* budget, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream);
+
+/* Flash block-sparse attention ("Flash Block-Sparse Attention"): for every
+ * query token of Q block i, softmax(scale * q K_sel^T) V_sel over all tokens of
+ * the KV blocks listed in CSR row i, written to o [B, H, N, d] in Q's dtype.
+ * Any CSR is accepted: ids outside [0, nblk), row extents outside
+ * [0, col_capacity] or decreasing row_ptr are skipped (never read out of
+ * bounds); a row with no valid block writes zeros. */
+spade_status spade_block_sparse_attn(const spade_problem* p, const void* q, const void* k, const void* v,
+                                     const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                                     void* o, void* workspace, size_t ws_bytes, void* stream);
+
+/* The whole path: summarize -> estimate/select -> block-sparse attention.
+ * Also returns the CSR it used in row_ptr / col_idx (capacity as above). */
+spade_status spade_attn(const spade_problem* p, const void* q, const void* k, const void* v,
+                        const spade_budget* budget, void* o, int32_t* row_ptr, int32_t* col_idx,
+                        int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream);
+
+/* Test hook: the fp64 scores S [B, H, nblk, nblk] that estimate/select uses. */
+spade_status spade_debug_scores(const spade_problem* p, const float* q_mean, const float* k_mean,
+                                double* scores, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPADE_H */

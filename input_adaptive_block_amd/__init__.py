@@ -1,0 +1,136 @@
+"""Input-adaptive block-sparse attention over 3D-blocked video tokens on MI355X.
+
+The compute lives in libspade.so (hand-written HIP kernels for gfx950 behind a
+C ABI, include/spade.h).  This package is its Python binding: `_lib` mirrors the
+C entry points one to one; the helpers below only allocate outputs and
+workspace with torch (device memory and streams) and forward to them.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+from ._lib import (  # noqa: F401
+    EXPORTED, LIB_PATH, MODES, Budget, Problem, SpadeError, SPADE_BF16, SPADE_F32,
+    SPADE_KEEP_COUNT, SPADE_KEEP_MASS, SPADE_KEEP_RATIO, SPADE_OK, SPADE_ERR_CAPACITY,
+    SPADE_ERR_DEVICE, SPADE_ERR_INVALID_ARG, SPADE_ERR_UNSUPPORTED, lib, spade_attn,
+    spade_block_sparse_attn, spade_check, spade_debug_scores, spade_estimate_select,
+    spade_max_nnz, spade_num_blocks, spade_summarize, spade_workspace_bytes, status_string,
+)
+
+__all__ = [
+    "Problem", "Budget", "SpadeError", "problem_for", "summarize", "estimate_select",
+    "block_sparse_attn", "attn", "debug_scores", "alloc_workspace",
+    "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
+    "spade_summarize", "spade_estimate_select", "spade_block_sparse_attn", "spade_attn",
+    "spade_debug_scores",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def problem_for(q, grid: Sequence[int], block: Sequence[int], scale: Optional[float] = None) -> Problem:
+    """Problem of a [B, H, N, d] tensor on grid (T, Hh, W) with block (bt, bh, bw)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    if q.dtype == torch.bfloat16:
+        dt = SPADE_BF16
+    elif q.dtype == torch.float32:
+        dt = SPADE_F32
+    else:
+        raise SpadeError(SPADE_ERR_UNSUPPORTED, f"dtype {q.dtype}")
+    T, Hh, W = grid
+    bt, bh, bw = block
+    return Problem(B, H, N, d, T, Hh, W, bt, bh, bw, dt, 0.0 if scale is None else float(scale))
+
+
+def _check_tensor(t, name, shape=None, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def alloc_workspace(problem: Problem, device=None):
+    torch = _torch()
+    n = spade_workspace_bytes(problem)
+    if n == 0:
+        raise SpadeError(spade_check(problem), "spade_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def summarize(q, k, grid, block) -> Tuple["object", "object"]:
+    torch = _torch()
+    p = problem_for(q, grid, block)
+    nblk = spade_num_blocks(p)
+    if nblk < 0:
+        raise SpadeError(spade_check(p), "summarize")
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", q.shape, q.dtype)
+    qm = torch.empty(p.B, p.H, nblk, p.d, dtype=torch.float32, device=q.device)
+    km = torch.empty_like(qm)
+    spade_summarize(p, q, k, qm, km)
+    return qm, km
+
+
+def estimate_select(q_mean, k_mean, problem: Problem, mode, per_head: Sequence[float], workspace=None):
+    torch = _torch()
+    bud = Budget(mode, per_head)
+    cap = spade_max_nnz(problem, bud)
+    if cap < 0:
+        raise SpadeError(spade_check(problem, bud), "estimate_select")
+    nblk = spade_num_blocks(problem)
+    R = problem.B * problem.H * nblk
+    row_ptr = torch.empty(R + 1, dtype=torch.int32, device=q_mean.device)
+    col_idx = torch.empty(max(1, cap), dtype=torch.int32, device=q_mean.device)
+    ws = alloc_workspace(problem, q_mean.device) if workspace is None else workspace
+    spade_estimate_select(problem, q_mean, k_mean, bud, row_ptr, col_idx, cap, ws, ws.numel())
+    return row_ptr, col_idx
+
+
+def block_sparse_attn(q, k, v, grid, block, row_ptr, col_idx, scale=None, workspace=None, out=None):
+    torch = _torch()
+    p = problem_for(q, grid, block, scale)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name, q.shape, q.dtype)
+    _check_tensor(row_ptr, "row_ptr", dtype=torch.int32)
+    _check_tensor(col_idx, "col_idx", dtype=torch.int32)
+    o = torch.empty_like(q) if out is None else out
+    ws = alloc_workspace(p, q.device) if workspace is None else workspace
+    spade_block_sparse_attn(p, q, k, v, row_ptr, col_idx, col_idx.numel(), o, ws, ws.numel())
+    return o
+
+
+def attn(q, k, v, grid, block, mode, per_head: Sequence[float], scale=None, workspace=None):
+    """Whole path; returns (o, row_ptr, col_idx)."""
+    torch = _torch()
+    p = problem_for(q, grid, block, scale)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name, q.shape, q.dtype)
+    bud = Budget(mode, per_head)
+    cap = spade_max_nnz(p, bud)
+    if cap < 0:
+        raise SpadeError(spade_check(p, bud), "attn")
+    nblk = spade_num_blocks(p)
+    R = p.B * p.H * nblk
+    row_ptr = torch.empty(R + 1, dtype=torch.int32, device=q.device)
+    col_idx = torch.empty(max(1, cap), dtype=torch.int32, device=q.device)
+    o = torch.empty_like(q)
+    ws = alloc_workspace(p, q.device) if workspace is None else workspace
+    spade_attn(p, q, k, v, bud, o, row_ptr, col_idx, cap, ws, ws.numel())
+    return o, row_ptr, col_idx
+
+
+def debug_scores(q_mean, k_mean, problem: Problem):
+    torch = _torch()
+    nblk = spade_num_blocks(problem)
+    S = torch.empty(problem.B, problem.H, nblk, nblk, dtype=torch.float64, device=q_mean.device)
+    spade_debug_scores(problem, q_mean, k_mean, S)
+    return S

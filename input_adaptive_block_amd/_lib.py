@@ -1,0 +1,207 @@
+"""ctypes binding of libspade.so (argument marshalling only).
+
+Every function here forwards to the C entry point of the same name declared
+in include/spade.h; all computation happens in the library's HIP kernels.
+There is no fallback: if the shared library is missing the import of the
+binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspade.so")
+
+SPADE_OK = 0
+SPADE_ERR_INVALID_ARG = 1
+SPADE_ERR_UNSUPPORTED = 2
+SPADE_ERR_CAPACITY = 3
+SPADE_ERR_DEVICE = 4
+
+SPADE_BF16 = 0
+SPADE_F32 = 1
+
+SPADE_KEEP_COUNT = 0
+SPADE_KEEP_RATIO = 1
+SPADE_KEEP_MASS = 2
+
+MODES = {"count": SPADE_KEEP_COUNT, "ratio": SPADE_KEEP_RATIO, "mass": SPADE_KEEP_MASS}
+
+
+class SpadeError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("T", ctypes.c_int32), ("Hh", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("bt", ctypes.c_int32), ("bh", ctypes.c_int32), ("bw", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+    ]
+
+
+class _Budget(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("per_head", ctypes.POINTER(ctypes.c_float))]
+
+
+@dataclass(frozen=True)
+class Problem:
+    B: int
+    H: int
+    N: int
+    d: int
+    T: int
+    Hh: int
+    W: int
+    bt: int
+    bh: int
+    bw: int
+    dtype: int = SPADE_BF16
+    scale: float = 0.0
+
+    def c(self) -> _Problem:
+        return _Problem(self.B, self.H, self.N, self.d, self.T, self.Hh, self.W,
+                        self.bt, self.bh, self.bw, self.dtype, self.scale)
+
+
+class Budget:
+    """Per-head keep budget (host memory, kept alive with the object)."""
+
+    def __init__(self, mode, per_head: Sequence[float]):
+        self.mode = MODES[mode] if isinstance(mode, str) else int(mode)
+        self.values = (ctypes.c_float * max(1, len(per_head)))(*[float(v) for v in per_head])
+        self._c = _Budget(self.mode, ctypes.cast(self.values, ctypes.POINTER(ctypes.c_float)))
+
+    def c(self) -> _Budget:
+        return self._c
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python input_adaptive_block_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(_Problem)
+    Bp = ctypes.POINTER(_Budget)
+    vp = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    sz = ctypes.c_size_t
+    st = ctypes.c_int
+    sig = {
+        "spade_num_blocks": (ctypes.c_int32, [P]),
+        "spade_max_nnz": (i64, [P, Bp]),
+        "spade_workspace_bytes": (sz, [P]),
+        "spade_check": (st, [P, Bp, i64]),
+        "spade_status_string": (ctypes.c_char_p, [st]),
+        "spade_summarize": (st, [P, vp, vp, vp, vp, vp]),
+        "spade_estimate_select": (st, [P, vp, vp, Bp, vp, vp, i64, vp, sz, vp]),
+        "spade_block_sparse_attn": (st, [P, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
+        "spade_attn": (st, [P, vp, vp, vp, Bp, vp, vp, vp, i64, vp, sz, vp]),
+        "spade_debug_scores": (st, [P, vp, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_LIB = _load()
+
+EXPORTED = (
+    "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
+    "spade_status_string", "spade_summarize", "spade_estimate_select",
+    "spade_block_sparse_attn", "spade_attn", "spade_debug_scores",
+)
+
+
+def lib() -> ctypes.CDLL:
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return _LIB.spade_status_string(int(status)).decode()
+
+
+def _ref(x):
+    return ctypes.byref(x) if x is not None else None
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != SPADE_OK:
+        raise SpadeError(status, where)
+
+
+def spade_num_blocks(problem: Problem) -> int:
+    return _LIB.spade_num_blocks(ctypes.byref(problem.c()))
+
+
+def spade_max_nnz(problem: Problem, budget: Budget) -> int:
+    return _LIB.spade_max_nnz(ctypes.byref(problem.c()), _ref(budget.c()))
+
+
+def spade_workspace_bytes(problem: Problem) -> int:
+    return _LIB.spade_workspace_bytes(ctypes.byref(problem.c()))
+
+
+def spade_check(problem: Problem, budget: Optional[Budget] = None, col_capacity: int = -1) -> int:
+    return _LIB.spade_check(ctypes.byref(problem.c()), None if budget is None else ctypes.byref(budget.c()),
+                            int(col_capacity))
+
+
+def spade_summarize(problem: Problem, q, k, q_mean, k_mean, stream=None) -> None:
+    _check(_LIB.spade_summarize(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(q_mean), _ptr(k_mean),
+                                _stream(stream)), "spade_summarize")
+
+
+def spade_estimate_select(problem: Problem, q_mean, k_mean, budget: Budget, row_ptr, col_idx,
+                          col_capacity: int, workspace, ws_bytes: int, stream=None) -> None:
+    _check(_LIB.spade_estimate_select(ctypes.byref(problem.c()), _ptr(q_mean), _ptr(k_mean),
+                                      ctypes.byref(budget.c()), _ptr(row_ptr), _ptr(col_idx),
+                                      int(col_capacity), _ptr(workspace), int(ws_bytes), _stream(stream)),
+           "spade_estimate_select")
+
+
+def spade_block_sparse_attn(problem: Problem, q, k, v, row_ptr, col_idx, col_capacity: int, o,
+                            workspace, ws_bytes: int, stream=None) -> None:
+    _check(_LIB.spade_block_sparse_attn(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
+                                        _ptr(col_idx), int(col_capacity), _ptr(o), _ptr(workspace),
+                                        int(ws_bytes), _stream(stream)),
+           "spade_block_sparse_attn")
+
+
+def spade_attn(problem: Problem, q, k, v, budget: Budget, o, row_ptr, col_idx, col_capacity: int,
+               workspace, ws_bytes: int, stream=None) -> None:
+    _check(_LIB.spade_attn(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(budget.c()),
+                           _ptr(o), _ptr(row_ptr), _ptr(col_idx), int(col_capacity), _ptr(workspace),
+                           int(ws_bytes), _stream(stream)),
+           "spade_attn")
+
+
+def spade_debug_scores(problem: Problem, q_mean, k_mean, scores, stream=None) -> None:
+    _check(_LIB.spade_debug_scores(ctypes.byref(problem.c()), _ptr(q_mean), _ptr(k_mean), _ptr(scores),
+                                   _stream(stream)), "spade_debug_scores")

@@ -1,0 +1,304 @@
+// Host side of the C ABI: validation, workspace carve-up and the launch
+// sequence of each entry point (all kernels on the caller's stream).
+#include <math.h>
+#include <string.h>
+
+#include "../../include/spade.h"
+#include "spade_internal.h"
+
+namespace spade {
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Fill g from p; returns SPADE_OK or the reason the shape is rejected.
+spade_status make_geom(const spade_problem* p, Geom* g) {
+  if (p == nullptr) return SPADE_ERR_INVALID_ARG;
+  if (p->B < 0 || p->H < 0 || p->d <= 0) return SPADE_ERR_INVALID_ARG;
+  if (p->T <= 0 || p->Hh <= 0 || p->W <= 0) return SPADE_ERR_INVALID_ARG;
+  if (p->bt <= 0 || p->bh <= 0 || p->bw <= 0) return SPADE_ERR_INVALID_ARG;
+  if (p->dtype != SPADE_BF16 && p->dtype != SPADE_F32) return SPADE_ERR_INVALID_ARG;
+  if (!(p->scale >= 0.0f) || isinf(p->scale)) return SPADE_ERR_INVALID_ARG;  // NaN, <0, inf
+  const long long N = (long long)p->T * p->Hh * p->W;
+  if (N != (long long)p->N) return SPADE_ERR_INVALID_ARG;
+  if (p->d != 64 && p->d != 128) return SPADE_ERR_UNSUPPORTED;
+  if (p->H > kMaxHeads) return SPADE_ERR_UNSUPPORTED;
+  const int bt = p->bt < p->T ? p->bt : p->T;
+  const int bh = p->bh < p->Hh ? p->bh : p->Hh;
+  const int bw = p->bw < p->W ? p->bw : p->W;
+  const long long ntok = (long long)bt * bh * bw;
+  if (ntok > kMaxBlockTokens) return SPADE_ERR_UNSUPPORTED;
+  const long long nT = (p->T + p->bt - 1) / p->bt, nH = (p->Hh + p->bh - 1) / p->bh,
+                  nW = (p->W + p->bw - 1) / p->bw;
+  const long long nblk = nT * nH * nW;
+  if (nblk > kMaxBlocks) return SPADE_ERR_UNSUPPORTED;
+  const long long BH = (long long)p->B * p->H;
+  const long long R = BH * nblk;
+  const int P = (int)((ntok + 31) / 32 * 32);
+  if (R * ((P + 127) / 128) >= (1LL << 31)) return SPADE_ERR_UNSUPPORTED;
+  if (BH * N * p->d >= (1LL << 50)) return SPADE_ERR_UNSUPPORTED;
+  g->B = p->B; g->H = p->H; g->N = p->N; g->d = p->d;
+  g->T = p->T; g->Hh = p->Hh; g->W = p->W;
+  g->bt = p->bt; g->bh = p->bh; g->bw = p->bw;
+  g->nT = (int)nT; g->nH = (int)nH; g->nW = (int)nW; g->nblk = (int)nblk;
+  g->ntok = (int)ntok;
+  g->P = P;
+  g->BH = (int)BH;
+  g->R = (int)R;
+  g->bf16 = p->dtype == SPADE_BF16 ? 1 : 0;
+  return SPADE_OK;
+}
+
+// Blocks per row for COUNT / RATIO (host arithmetic in double).
+int keep_k(int mode, float v, int nblk) {
+  if (mode == SPADE_KEEP_COUNT) return (int)v;
+  long long k = (long long)ceil((double)v * nblk - 1e-6);
+  if (k < 1) k = 1;
+  if (k > nblk) k = nblk;
+  return (int)k;
+}
+
+spade_status check_budget(const spade_budget* bgt, const Geom& g) {
+  if (bgt == nullptr) return SPADE_ERR_INVALID_ARG;
+  if (bgt->mode != SPADE_KEEP_COUNT && bgt->mode != SPADE_KEEP_RATIO && bgt->mode != SPADE_KEEP_MASS)
+    return SPADE_ERR_INVALID_ARG;
+  if (g.H > 0 && bgt->per_head == nullptr) return SPADE_ERR_INVALID_ARG;
+  for (int h = 0; h < g.H; ++h) {
+    const float v = bgt->per_head[h];
+    if (!(v == v) || isinf(v)) return SPADE_ERR_INVALID_ARG;
+    if (bgt->mode == SPADE_KEEP_COUNT) {
+      if (v != floorf(v) || v < 1.0f || v > (float)g.nblk) return SPADE_ERR_INVALID_ARG;
+    } else if (!(v > 0.0f && v <= 1.0f)) {
+      return SPADE_ERR_INVALID_ARG;
+    }
+  }
+  return SPADE_OK;
+}
+
+long long max_nnz(const Geom& g, const spade_budget* bgt) {
+  if (bgt->mode == SPADE_KEEP_MASS) return (long long)g.R * g.nblk;
+  long long per_batch = 0;
+  for (int h = 0; h < g.H; ++h) per_batch += keep_k(bgt->mode, bgt->per_head[h], g.nblk);
+  return per_batch * g.nblk * g.B;
+}
+
+int num_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+inline float attn_scale(const spade_problem* p) {
+  return p->scale > 0.0f ? p->scale : (float)(1.0 / sqrt((double)p->d));
+}
+
+inline double est_scale(const spade_problem* p) {
+  return p->scale > 0.0f ? (double)p->scale : 1.0 / sqrt((double)p->d);
+}
+
+inline spade_status dev(hipError_t e) { return e == hipSuccess ? SPADE_OK : SPADE_ERR_DEVICE; }
+
+#define SPADE_TRY(expr)                       \
+  do {                                        \
+    const spade_status st_ = (expr);          \
+    if (st_ != SPADE_OK) return st_;          \
+  } while (0)
+
+SelectArgs make_select_args(const spade_budget* bgt, const Geom& g) {
+  SelectArgs a;
+  memset(&a, 0, sizeof(a));
+  a.mode = bgt->mode;
+  for (int h = 0; h < g.H; ++h) {
+    if (bgt->mode == SPADE_KEEP_MASS)
+      a.tau[h] = (double)bgt->per_head[h];
+    else
+      a.k[h] = keep_k(bgt->mode, bgt->per_head[h], g.nblk);
+  }
+  return a;
+}
+
+char* ws_ptr(void* ws, size_t off) { return reinterpret_cast<char*>(ws) + off; }
+
+spade_status run_select(const spade_problem* p, const Geom& g, const Workspace& L, const float* qm,
+                        const float* km, const spade_budget* bgt, int* row_ptr, int* col_idx, void* ws,
+                        hipStream_t s) {
+  double* scores = reinterpret_cast<double*>(ws_ptr(ws, L.scores));
+  int* counts = reinterpret_cast<int*>(ws_ptr(ws, L.counts));
+  uint32_t* mask = reinterpret_cast<uint32_t*>(ws_ptr(ws, L.mask));
+  SPADE_TRY(dev(launch_scores(g, qm, km, est_scale(p), scores, s)));
+  const SelectArgs a = make_select_args(bgt, g);
+  SPADE_TRY(dev(launch_select(g, scores, a, counts, mask, L.mask_words, s)));
+  SPADE_TRY(dev(launch_scan(g, counts, row_ptr, s)));
+  SPADE_TRY(dev(launch_compact(g, row_ptr, mask, L.mask_words, col_idx, s)));
+  return SPADE_OK;
+}
+
+}  // namespace
+
+Workspace workspace_layout(const Geom& g) {
+  Workspace L;
+  size_t off = 0;
+  L.mask_words = (g.nblk + 31) / 32;
+  L.counts = off; off = align256(off + (size_t)g.R * 4);
+  L.mask = off; off = align256(off + (size_t)g.R * L.mask_words * 4);
+  L.scores = off; off = align256(off + (size_t)g.R * g.nblk * 8);
+  L.qmean = off; off = align256(off + (size_t)g.BH * g.nblk * g.d * 4);
+  L.kmean = off; off = align256(off + (size_t)g.BH * g.nblk * g.d * 4);
+  const size_t pack = g.bf16 ? (size_t)g.BH * g.nblk * g.P * g.d * 2 : 0;
+  L.qpack = off; off = align256(off + pack);
+  L.kpack = off; off = align256(off + pack);
+  L.vpack = off; off = align256(off + pack);
+  L.queue = off; off = align256(off + (2 * kQueues + 2) * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace spade
+
+using namespace spade;
+
+extern "C" {
+
+int32_t spade_num_blocks(const spade_problem* p) {
+  Geom g;
+  if (make_geom(p, &g) != SPADE_OK) return -1;
+  return g.nblk;
+}
+
+int64_t spade_max_nnz(const spade_problem* p, const spade_budget* budget) {
+  Geom g;
+  if (make_geom(p, &g) != SPADE_OK) return -1;
+  if (check_budget(budget, g) != SPADE_OK) return -1;
+  return max_nnz(g, budget);
+}
+
+size_t spade_workspace_bytes(const spade_problem* p) {
+  Geom g;
+  if (make_geom(p, &g) != SPADE_OK) return 0;
+  return workspace_layout(g).total;
+}
+
+spade_status spade_check(const spade_problem* p, const spade_budget* budget, int64_t col_capacity) {
+  Geom g;
+  SPADE_TRY(make_geom(p, &g));
+  if (budget != nullptr) {
+    SPADE_TRY(check_budget(budget, g));
+    const long long need = max_nnz(g, budget);
+    if (need >= (1LL << 31)) return SPADE_ERR_UNSUPPORTED;
+    if (col_capacity >= 0 && col_capacity < need) return SPADE_ERR_CAPACITY;
+  }
+  return SPADE_OK;
+}
+
+const char* spade_status_string(spade_status s) {
+  switch (s) {
+    case SPADE_OK: return "SPADE_OK";
+    case SPADE_ERR_INVALID_ARG: return "SPADE_ERR_INVALID_ARG";
+    case SPADE_ERR_UNSUPPORTED: return "SPADE_ERR_UNSUPPORTED";
+    case SPADE_ERR_CAPACITY: return "SPADE_ERR_CAPACITY";
+    case SPADE_ERR_DEVICE: return "SPADE_ERR_DEVICE";
+  }
+  return "SPADE_ERR_UNKNOWN";
+}
+
+spade_status spade_summarize(const spade_problem* p, const void* q, const void* k, float* q_mean,
+                             float* k_mean, void* stream) {
+  Geom g;
+  SPADE_TRY(make_geom(p, &g));
+  if (g.BH == 0) return SPADE_OK;
+  if (!q || !k || !q_mean || !k_mean) return SPADE_ERR_INVALID_ARG;
+  return dev(launch_summarize(g, p->dtype == SPADE_BF16, q, k, nullptr, q_mean, k_mean, nullptr, nullptr,
+                              nullptr, (hipStream_t)stream));
+}
+
+spade_status spade_estimate_select(const spade_problem* p, const float* q_mean, const float* k_mean,
+                                   const spade_budget* budget, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream) {
+  Geom g;
+  SPADE_TRY(make_geom(p, &g));
+  SPADE_TRY(check_budget(budget, g));
+  const long long need = max_nnz(g, budget);
+  if (need >= (1LL << 31)) return SPADE_ERR_UNSUPPORTED;
+  if (col_capacity < need) return SPADE_ERR_CAPACITY;
+  if (!row_ptr) return SPADE_ERR_INVALID_ARG;
+  const Workspace L = workspace_layout(g);
+  if (ws_bytes < L.total) return SPADE_ERR_CAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  if (g.R == 0) return dev(launch_scan(g, nullptr, row_ptr, s));
+  if (!q_mean || !k_mean || !col_idx || !workspace) return SPADE_ERR_INVALID_ARG;
+  return run_select(p, g, L, q_mean, k_mean, budget, row_ptr, col_idx, workspace, s);
+}
+
+spade_status spade_block_sparse_attn(const spade_problem* p, const void* q, const void* k, const void* v,
+                                     const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                                     void* o, void* workspace, size_t ws_bytes, void* stream) {
+  Geom g;
+  SPADE_TRY(make_geom(p, &g));
+  if (col_capacity < 0) return SPADE_ERR_INVALID_ARG;
+  const Workspace L = workspace_layout(g);
+  if (ws_bytes < L.total) return SPADE_ERR_CAPACITY;
+  if (g.R == 0) return SPADE_OK;
+  if (!q || !k || !v || !row_ptr || !o || !workspace) return SPADE_ERR_INVALID_ARG;
+  if (col_capacity > 0 && !col_idx) return SPADE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const float scale = attn_scale(p);
+  if (p->dtype == SPADE_BF16) {
+    void* qp = ws_ptr(workspace, L.qpack);
+    void* kp = ws_ptr(workspace, L.kpack);
+    void* vp = ws_ptr(workspace, L.vpack);
+    SPADE_TRY(dev(launch_summarize(g, true, q, k, v, nullptr, nullptr, qp, kp, vp, s)));
+    return dev(launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o,
+                                  reinterpret_cast<int*>(ws_ptr(workspace, L.queue)), num_cus(), s));
+  }
+  return dev(launch_bsattn_f32(g, (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
+                               col_capacity, scale, (float*)o, s));
+}
+
+spade_status spade_attn(const spade_problem* p, const void* q, const void* k, const void* v,
+                        const spade_budget* budget, void* o, int32_t* row_ptr, int32_t* col_idx,
+                        int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream) {
+  Geom g;
+  SPADE_TRY(make_geom(p, &g));
+  SPADE_TRY(check_budget(budget, g));
+  const long long need = max_nnz(g, budget);
+  if (need >= (1LL << 31)) return SPADE_ERR_UNSUPPORTED;
+  if (col_capacity < need) return SPADE_ERR_CAPACITY;
+  const Workspace L = workspace_layout(g);
+  if (ws_bytes < L.total) return SPADE_ERR_CAPACITY;
+  if (!row_ptr) return SPADE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (g.R == 0) return dev(launch_scan(g, nullptr, row_ptr, s));
+  if (!q || !k || !v || !o || !col_idx || !workspace) return SPADE_ERR_INVALID_ARG;
+  float* qm = reinterpret_cast<float*>(ws_ptr(workspace, L.qmean));
+  float* km = reinterpret_cast<float*>(ws_ptr(workspace, L.kmean));
+  const float scale = attn_scale(p);
+  if (p->dtype == SPADE_BF16) {
+    void* qp = ws_ptr(workspace, L.qpack);
+    void* kp = ws_ptr(workspace, L.kpack);
+    void* vp = ws_ptr(workspace, L.vpack);
+    SPADE_TRY(dev(launch_summarize(g, true, q, k, v, qm, km, qp, kp, vp, s)));
+    SPADE_TRY(run_select(p, g, L, qm, km, budget, row_ptr, col_idx, workspace, s));
+    return dev(launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o,
+                                  reinterpret_cast<int*>(ws_ptr(workspace, L.queue)), num_cus(), s));
+  }
+  SPADE_TRY(dev(launch_summarize(g, false, q, k, nullptr, qm, km, nullptr, nullptr, nullptr, s)));
+  SPADE_TRY(run_select(p, g, L, qm, km, budget, row_ptr, col_idx, workspace, s));
+  return dev(launch_bsattn_f32(g, (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
+                               col_capacity, scale, (float*)o, s));
+}
+
+spade_status spade_debug_scores(const spade_problem* p, const float* q_mean, const float* k_mean,
+                                double* scores, void* stream) {
+  Geom g;
+  SPADE_TRY(make_geom(p, &g));
+  if (g.BH == 0) return SPADE_OK;
+  if (!q_mean || !k_mean || !scores) return SPADE_ERR_INVALID_ARG;
+  return dev(launch_scores(g, q_mean, k_mean, est_scale(p), scores, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Internal declarations shared by the HIP kernels and the host API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spade {
+
+constexpr int kMaxHeads = 256;     // per-head budgets travel as kernel arguments
+constexpr int kMaxBlocks = 4096;   // nblk limit (selection keeps a row in registers)
+constexpr int kMaxBlockTokens = 1024;
+constexpr int kQueues = 8;         // one work queue per XCD of the MI355X
+
+// Geometry of one problem, valid on host and device.
+struct Geom {
+  int B, H, N, d;
+  int T, Hh, W;
+  int bt, bh, bw;
+  int nT, nH, nW, nblk;
+  int ntok;   // bt*bh*bw, tokens of a full block
+  int P;      // ntok rounded up to a multiple of 32 (padded tile rows)
+  int BH;     // B*H
+  int R;      // B*H*nblk selection rows
+  int bf16;   // 1: bf16 tensors (packed MFMA tiles), 0: fp32 debug path
+};
+
+struct BlockBox {
+  int t0, h0, w0;  // origin
+  int et, eh, ew;  // extents (partial at the far edges)
+  int n;           // et*eh*ew
+};
+
+__host__ __device__ inline BlockBox block_box(const Geom& g, int j) {
+  BlockBox b;
+  int it = j / (g.nH * g.nW);
+  int rem = j - it * g.nH * g.nW;
+  int ih = rem / g.nW;
+  int iw = rem - ih * g.nW;
+  b.t0 = it * g.bt;
+  b.h0 = ih * g.bh;
+  b.w0 = iw * g.bw;
+  b.et = min(g.bt, g.T - b.t0);
+  b.eh = min(g.bh, g.Hh - b.h0);
+  b.ew = min(g.bw, g.W - b.w0);
+  b.n = b.et * b.eh * b.ew;
+  return b;
+}
+
+// Raster token of local index l (t-major, then h, then w) inside block b.
+__host__ __device__ inline int block_token(const Geom& g, const BlockBox& b, int l) {
+  int ehw = b.eh * b.ew;
+  int lt = l / ehw;
+  int r = l - lt * ehw;
+  int lh = r / b.ew;
+  int lw = r - lh * b.ew;
+  return ((b.t0 + lt) * g.Hh + (b.h0 + lh)) * g.W + (b.w0 + lw);
+}
+
+// Budget as passed to the selection kernel (by value).
+struct SelectArgs {
+  int mode;              // spade_keep_mode
+  int k[kMaxHeads];      // COUNT / RATIO: blocks per row of head h
+  double tau[kMaxHeads]; // MASS: threshold of head h
+};
+
+// Workspace carve-up (byte offsets, 256-aligned).
+struct Workspace {
+  size_t counts;    // int32 [R]
+  size_t mask;      // uint32 [R * mask_words]
+  size_t scores;    // double [R * nblk]
+  size_t qmean;     // float [BH * nblk * d]
+  size_t kmean;     // float [BH * nblk * d]
+  size_t qpack;     // bf16 [BH * nblk * P * d]
+  size_t kpack;
+  size_t vpack;
+  size_t queue;     // int32 [2 * kQueues + 2]
+  size_t total;
+  int mask_words;
+};
+
+Workspace workspace_layout(const Geom& g);
+
+// ---- launchers (each returns hipSuccess or the launch error) -------------
+hipError_t launch_summarize(const Geom& g, bool bf16, const void* q, const void* k, const void* v,
+                            float* q_mean, float* k_mean, void* qpack, void* kpack, void* vpack,
+                            hipStream_t s);
+hipError_t launch_scores(const Geom& g, const float* q_mean, const float* k_mean, double scale,
+                         double* scores, hipStream_t s);
+hipError_t launch_select(const Geom& g, const double* scores, const SelectArgs& a, int* counts,
+                         uint32_t* mask, int mask_words, hipStream_t s);
+hipError_t launch_scan(const Geom& g, const int* counts, int* row_ptr, hipStream_t s);
+hipError_t launch_compact(const Geom& g, const int* row_ptr, const uint32_t* mask, int mask_words,
+                          int* col_idx, hipStream_t s);
+hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpack, const void* vpack,
+                              const int* row_ptr, const int* col_idx, long long col_capacity,
+                              float scale, void* o, int* queue, int num_cus, hipStream_t s);
+hipError_t launch_bsattn_f32(const Geom& g, const float* q, const float* k, const float* v,
+                             const int* row_ptr, const int* col_idx, long long col_capacity,
+                             float scale, float* o, hipStream_t s);
+
+}  // namespace spade

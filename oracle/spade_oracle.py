@@ -236,6 +236,9 @@ def attention_block_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, toks: List[
     """
     kept = list(kept)
     qi = q[toks[i]]
+    if not kept:  # reading: a row that keeps no block attends to nothing -> zeros
+        z = np.zeros((len(toks[i]), v.shape[1]))
+        return (z, np.zeros((len(toks[i]), 0)), np.zeros(0, np.int64)) if return_weights else z
     key_ids = np.concatenate([toks[j] for j in kept])
     logits = scale * (qi @ k[key_ids].T)
     logits = logits - logits.max(axis=1, keepdims=True)

@@ -1,0 +1,326 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (block-sparse attention contract):
+* summaries: the GPU's fp32 means equal the oracle's exact means rounded to
+  fp32 (at most one fp32 ulp apart);
+* scores: fp64 on both sides, |dS| <= 1e-12 * max(1, |S|max);
+* block indices: identical to the oracle's on every row whose oracle margin
+  exceeds 1e-3 (the contract) -- and, since both sides decide in fp64, on
+  every row whose margin exceeds 1e-9; the oracle's selection run on the GPU's
+  own scores reproduces the GPU's CSR on every row;
+* outputs, computed with the GPU's CSR fed to the oracle: max-abs error
+  <= 2e-2 for bf16 and <= 1e-5 for the fp32 debug path.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only hosts, skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import input_adaptive_block_amd as spade  # noqa: E402
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-5
+SMALL = ["tiny", "tiny_bf16", "ragged_p64", "mid_shape", "small_shape", "ragged_small", "big_block",
+         "token_level", "one_block", "d64", "ragged_f32"]
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def geom(cfg):
+    return oracle.Geometry(cfg.T, cfg.Hh, cfg.W, cfg.bt, cfg.bh, cfg.bw)
+
+
+def to_dev(cfg, a):
+    if cfg.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_f64(cfg, a):
+    return synth.bf16_bits_to_f64(a) if cfg.dtype == "bf16" else a.astype(np.float64)
+
+
+def dev_to_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def grid_block(cfg):
+    return (cfg.T, cfg.Hh, cfg.W), (cfg.bt, cfg.bh, cfg.bw)
+
+
+def oracle_means(cfg, x):
+    """Oracle block means per head chunk (bounded host memory)."""
+    g = geom(cfg)
+    out = np.empty((cfg.B, cfg.H, g.nblk, cfg.d))
+    for h in range(cfg.H):
+        out[:, h:h + 1] = oracle.summarize(to_f64(cfg, x[:, h:h + 1]), g)
+    return out
+
+
+def csr_rows(row_ptr, col_idx):
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy().astype(np.int64)
+    return rp, ci
+
+
+def compare_selection(sel, rp, ci, S_ref, mode, budget, name):
+    """Contract check + strict fp64 check; returns number of differing rows."""
+    R = len(sel.counts)
+    assert rp.shape[0] == R + 1 and rp[0] == 0
+    diff = []
+    for r in range(R):
+        got = ci[rp[r]:rp[r + 1]]
+        if not np.array_equal(got, sel.row(r)):
+            diff.append(r)
+    for r in diff:
+        m = sel.margins[r]
+        assert m <= 1e-3, f"{name}: row {r} differs with oracle margin {m}"
+        assert m <= 1e-9, f"{name}: row {r} differs although both sides decide in fp64 (margin {m})"
+    return len(diff)
+
+
+def run_attn(cfg, x, mode=None, budget=None, scale=None):
+    grid, block = grid_block(cfg)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    mode = cfg.mode if mode is None else mode
+    budget = cfg.per_head_budget() if budget is None else budget
+    o, rp, ci = spade.attn(q, k, v, grid, block, mode, budget, scale=scale)
+    torch.cuda.synchronize()
+    return o, rp, ci
+
+
+# ---------------------------------------------------------------------------
+# small configurations, every row and every output element
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", SMALL)
+def test_summarize_matches_oracle(name):
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    qm, km = spade.summarize(to_dev(cfg, x["q"]), to_dev(cfg, x["k"]), grid, block)
+    for got, ref in ((qm, oracle_means(cfg, x["q"])), (km, oracle_means(cfg, x["k"]))):
+        g = got.cpu().numpy().astype(np.float64)
+        ulp = np.abs(ref) * 2.0 ** -23 + 1e-38
+        assert (np.abs(g - ref) <= ulp).all(), np.abs(g - ref).max()
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_scores_and_selection_match_oracle(name):
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    qd, kd = to_dev(cfg, x["q"]), to_dev(cfg, x["k"])
+    qm, km = spade.summarize(qd, kd, grid, block)
+    p = spade.problem_for(qd, grid, block)
+    S_gpu = spade.debug_scores(qm, km, p).cpu().numpy()
+    scale = oracle.default_scale(cfg.d)
+    S_from_gpu_means = oracle.estimate(qm.cpu().numpy().astype(np.float64),
+                                       km.cpu().numpy().astype(np.float64), scale)
+    tol = 1e-12 * max(1.0, np.abs(S_from_gpu_means).max())
+    assert np.abs(S_gpu - S_from_gpu_means).max() <= tol
+    S_ref = oracle.estimate(oracle_means(cfg, x["q"]), oracle_means(cfg, x["k"]), scale)
+    assert np.abs(S_gpu - S_ref).max() <= 1e-9 * max(1.0, np.abs(S_ref).max())
+
+    rp, ci = spade.estimate_select(qm, km, p, cfg.mode, cfg.per_head_budget())
+    rp, ci = csr_rows(rp, ci)
+    sel = oracle.select(S_ref, cfg.mode, cfg.per_head_budget())
+    ndiff = compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), name)
+    assert ndiff == 0
+    # logic check: the oracle's selection on the GPU's own scores
+    sel_g = oracle.select(S_gpu, cfg.mode, cfg.per_head_budget())
+    assert np.array_equal(sel_g.row_ptr, rp)
+    assert np.array_equal(sel_g.col_idx, ci[:rp[-1]])
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_attention_matches_oracle(name):
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    g = geom(cfg)
+    o, rp, ci = run_attn(cfg, x)
+    rp, ci = csr_rows(rp, ci)
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    scale = oracle.default_scale(cfg.d)
+    ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], g, rp, ci, scale)
+    err = np.abs(dev_to_f64(o) - ref).max()
+    assert err <= (BF16_TOL if cfg.dtype == "bf16" else F32_TOL), err
+    # and the CSR itself is the oracle's
+    S_ref = oracle.estimate(oracle_means(cfg, x["q"]), oracle_means(cfg, x["k"]), scale)
+    sel = oracle.select(S_ref, cfg.mode, cfg.per_head_budget())
+    assert compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), name) == 0
+
+
+@pytest.mark.parametrize("name", ["ragged_small", "ragged_p64", "tiny", "ragged_f32"])
+def test_ratio_one_equals_dense_attention(name):
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    o, rp, ci = run_attn(cfg, x, mode="ratio", budget=[1.0] * cfg.H)
+    g = geom(cfg)
+    assert (np.diff(rp.cpu().numpy()) == g.nblk).all()
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    ref = oracle.dense_attention(xf["q"], xf["k"], xf["v"], oracle.default_scale(cfg.d))
+    err = np.abs(dev_to_f64(o) - ref).max()
+    assert err <= (BF16_TOL if cfg.dtype == "bf16" else F32_TOL), err
+
+
+@pytest.mark.parametrize("name", ["mid_shape", "ragged_small", "tiny"])
+def test_block_sparse_attn_on_oracle_csr(name):
+    """spade_block_sparse_attn alone, fed the oracle's own CSR."""
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    g = geom(cfg)
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    scale = oracle.default_scale(cfg.d)
+    _, sel, _ = oracle.spade_attn(xf["q"], xf["k"], xf["v"], g, cfg.mode, cfg.per_head_budget())
+    grid, block = grid_block(cfg)
+    rp = torch.from_numpy(sel.row_ptr.astype(np.int32)).cuda()
+    ci = torch.from_numpy(sel.col_idx.astype(np.int32)).cuda()
+    o = spade.block_sparse_attn(*(to_dev(cfg, x[n]) for n in ("q", "k", "v")), grid, block, rp, ci)
+    ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], g, sel.row_ptr, sel.col_idx, scale)
+    err = np.abs(dev_to_f64(o) - ref).max()
+    assert err <= (BF16_TOL if cfg.dtype == "bf16" else F32_TOL), err
+
+
+@pytest.mark.parametrize("name", ["mid_shape", "tiny"])
+def test_arbitrary_csr_is_memory_safe(name):
+    """Duplicates count twice, invalid ids are skipped, empty rows give zeros."""
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    g = geom(cfg)
+    R = cfg.B * cfg.H * g.nblk
+    rng = np.random.default_rng(7)
+    rows, raw = [], []
+    for r in range(R):
+        if r % 5 == 2:
+            ids = []
+        else:
+            ids = sorted(rng.choice(g.nblk, size=min(g.nblk, 1 + r % 3), replace=False).tolist())
+            if r % 4 == 0:
+                ids = ids + [ids[0]]  # duplicate
+            if r % 3 == 0:
+                ids = [-1] + ids + [g.nblk + 5]  # out of range
+        raw.append(ids)
+        rows.append([j for j in ids if 0 <= j < g.nblk])
+    rp_raw = np.concatenate([[0], np.cumsum([len(a) for a in raw])]).astype(np.int32)
+    ci_raw = np.array([j for a in raw for j in a], dtype=np.int32)
+    rp_ok = np.concatenate([[0], np.cumsum([len(a) for a in rows])]).astype(np.int64)
+    ci_ok = np.array([j for a in rows for j in a], dtype=np.int64)
+    grid, block = grid_block(cfg)
+    o = spade.block_sparse_attn(*(to_dev(cfg, x[n]) for n in ("q", "k", "v")), grid, block,
+                                torch.from_numpy(rp_raw).cuda(), torch.from_numpy(ci_raw).cuda())
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], g, rp_ok, ci_ok, oracle.default_scale(cfg.d))
+    err = np.abs(dev_to_f64(o) - ref).max()
+    assert err <= (BF16_TOL if cfg.dtype == "bf16" else F32_TOL), err
+
+
+def test_scale_override():
+    cfg = synth.get_config("tiny")
+    x = synth.make_inputs(cfg)
+    o, rp, ci = run_attn(cfg, x, scale=0.05)
+    rp, ci = csr_rows(rp, ci)
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    s = float(np.float32(0.05))
+    _, sel, _ = oracle.spade_attn(xf["q"], xf["k"], xf["v"], geom(cfg), cfg.mode, cfg.per_head_budget(), scale=s)
+    assert np.array_equal(sel.col_idx, ci[:rp[-1]])
+    ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], geom(cfg), rp, ci, s)
+    assert np.abs(dev_to_f64(o) - ref).max() <= F32_TOL
+
+
+def test_zero_queries_select_lowest_ids():
+    cfg = synth.get_config("ragged_small")
+    x = synth.make_inputs(cfg)
+    x = dict(x, q=np.zeros_like(x["q"]))
+    g = geom(cfg)
+    for mode, val in (("ratio", 0.5), ("mass", 0.3)):
+        _, rp, ci = run_attn(cfg, x, mode=mode, budget=[val] * cfg.H)
+        rp, ci = csr_rows(rp, ci)
+        k = (oracle.keep_count("ratio", val, g.nblk) if mode == "ratio"
+             else math.ceil(float(np.float32(val)) * g.nblk))
+        for r in range(len(rp) - 1):
+            assert ci[rp[r]:rp[r + 1]].tolist() == list(range(k))
+
+
+def test_deterministic_and_writes_every_output_once():
+    cfg = synth.get_config("mid_shape")
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    p = spade.problem_for(q, grid, block)
+    bud = spade.Budget(cfg.mode, cfg.per_head_budget())
+    cap = spade.spade_max_nnz(p, bud)
+    nblk = spade.spade_num_blocks(p)
+    R = cfg.B * cfg.H * nblk
+    ws = spade.alloc_workspace(p, q.device)
+    G = 4096
+    outs = []
+    for _ in range(2):
+        big = torch.full((q.numel() + 2 * G,), float("nan"), dtype=q.dtype, device=q.device)
+        o = big[G:G + q.numel()].view(q.shape)
+        rp_big = torch.full((R + 1 + 2 * G,), -7, dtype=torch.int32, device=q.device)
+        ci_big = torch.full((cap + 2 * G,), -7, dtype=torch.int32, device=q.device)
+        rp = rp_big[G:G + R + 1]
+        ci = ci_big[G:G + cap]
+        spade.spade_attn(p, q, k, v, bud, o, rp, ci, cap, ws, ws.numel())
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all()
+        assert torch.isnan(big[:G].float()).all() and torch.isnan(big[-G:].float()).all()
+        assert (rp_big[:G] == -7).all() and (rp_big[-G:] == -7).all()
+        assert (ci_big[:G] == -7).all() and (ci_big[-G:] == -7).all()
+        outs.append((o.clone(), rp.clone(), ci[:int(rp[-1])].clone()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][2], outs[1][2])
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads in the bench's launch configuration: every row's block
+# set, sampled output rows
+# ---------------------------------------------------------------------------
+
+FULL = [("small", None), ("mid", None), ("large", None), ("ragged", 1.0), ("ragged", 0.5), ("ragged", 0.1)]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,ratio", FULL)
+def test_full_size_selection_and_sampled_rows(name, ratio):
+    cfg = synth.get_config(name)
+    if ratio is not None:
+        cfg = cfg.with_budget("ratio", ratio)
+    print(f"[full] {cfg.name}", flush=True)
+    x = synth.make_inputs(cfg)
+    g = geom(cfg)
+    o, rp, ci = run_attn(cfg, x)
+    rp, ci = csr_rows(rp, ci)
+    scale = oracle.default_scale(cfg.d)
+    S_ref = oracle.estimate(oracle_means(cfg, x["q"]), oracle_means(cfg, x["k"]), scale)
+    sel = oracle.select(S_ref, cfg.mode, cfg.per_head_budget())
+    ndiff = compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), cfg.name)
+    print(f"[full] {cfg.name}: rows {len(sel.counts)}, differing {ndiff}, "
+          f"ambiguous(m<=1e-3) {(sel.margins <= 1e-3).sum()}", flush=True)
+    R = len(sel.counts)
+    rng = np.random.default_rng(cfg.seed)
+    rows = sorted(set([0, R - 1] + rng.choice(R, size=6, replace=False).tolist()))
+    of = o.cpu()
+    toks = oracle.block_tokens(g)
+    worst = 0.0
+    for r in rows:
+        bh, i = divmod(r, g.nblk)
+        b, h = divmod(bh, cfg.H)
+        qh, kh, vh = (to_f64(cfg, x[n][b, h]) for n in ("q", "k", "v"))
+        ref = oracle.attention_block_row(qh, kh, vh, toks, i, ci[rp[r]:rp[r + 1]].tolist(), scale)
+        got = of[b, h, toks[i]].float().numpy().astype(np.float64)
+        worst = max(worst, np.abs(got - ref).max())
+    print(f"[full] {cfg.name}: sampled rows {rows} max-abs {worst:.3e}", flush=True)
+    assert worst <= BF16_TOL
