@@ -137,6 +137,13 @@ spade_status spade_attn(const spade_problem* p, const void* q, const void* k, co
                         const spade_budget* budget, void* o, int32_t* row_ptr, int32_t* col_idx,
                         int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream);
 
+/* Measurement hook for benchmarks: while both events (hipEvent_t) are
+ * non-NULL, every later spade_block_sparse_attn / spade_attn call on this host
+ * thread records `start` just before and `stop` just after its flash
+ * attention kernel, on the call's stream (the caller owns the events and reads
+ * them with hipEventElapsedTime).  Pass NULLs to turn recording off. */
+void spade_profile_events(void* start, void* stop);
+
 /* Test hook: the fp64 scores S [B, H, nblk, nblk] that estimate/select uses. */
 spade_status spade_debug_scores(const spade_problem* p, const float* q_mean, const float* k_mean,
                                 double* scores, void* stream);

@@ -14,7 +14,8 @@ from ._lib import (  # noqa: F401
     SPADE_KEEP_COUNT, SPADE_KEEP_MASS, SPADE_KEEP_RATIO, SPADE_OK, SPADE_ERR_CAPACITY,
     SPADE_ERR_DEVICE, SPADE_ERR_INVALID_ARG, SPADE_ERR_UNSUPPORTED, lib, spade_attn,
     spade_block_sparse_attn, spade_check, spade_debug_scores, spade_estimate_select,
-    spade_max_nnz, spade_num_blocks, spade_summarize, spade_workspace_bytes, status_string,
+    spade_max_nnz, spade_num_blocks, spade_profile_events, spade_summarize, spade_workspace_bytes,
+    status_string,
 )
 
 __all__ = [

@@ -83,6 +83,9 @@ class Budget:
 
 
 def _load() -> ctypes.CDLL:
+    # torch first: its HIP runtime is then the one libspade.so binds to, so
+    # torch's streams, events and allocations are valid handles for the library
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -105,6 +108,7 @@ def _load() -> ctypes.CDLL:
         "spade_block_sparse_attn": (st, [P, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
         "spade_attn": (st, [P, vp, vp, vp, Bp, vp, vp, vp, i64, vp, sz, vp]),
         "spade_debug_scores": (st, [P, vp, vp, vp, vp]),
+        "spade_profile_events": (None, [vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -118,7 +122,7 @@ _LIB = _load()
 EXPORTED = (
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
     "spade_status_string", "spade_summarize", "spade_estimate_select",
-    "spade_block_sparse_attn", "spade_attn", "spade_debug_scores",
+    "spade_block_sparse_attn", "spade_attn", "spade_debug_scores", "spade_profile_events",
 )
 
 
@@ -205,3 +209,8 @@ def spade_attn(problem: Problem, q, k, v, budget: Budget, o, row_ptr, col_idx, c
 def spade_debug_scores(problem: Problem, q_mean, k_mean, scores, stream=None) -> None:
     _check(_LIB.spade_debug_scores(ctypes.byref(problem.c()), _ptr(q_mean), _ptr(k_mean), _ptr(scores),
                                    _stream(stream)), "spade_debug_scores")
+
+
+def spade_profile_events(start, stop) -> None:
+    """Record hipEvent handles around every later attention kernel (None, None: off)."""
+    _LIB.spade_profile_events(start, stop)

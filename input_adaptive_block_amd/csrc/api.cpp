@@ -103,6 +103,18 @@ inline double est_scale(const spade_problem* p) {
 
 inline spade_status dev(hipError_t e) { return e == hipSuccess ? SPADE_OK : SPADE_ERR_DEVICE; }
 
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
+// The attention launch, bracketed by the measurement events when they are set.
+template <class F>
+spade_status timed_attention(hipStream_t s, F launch) {
+  if (g_prof_start && g_prof_stop && hipEventRecord(g_prof_start, s) != hipSuccess) return SPADE_ERR_DEVICE;
+  const hipError_t e = launch();
+  if (e != hipSuccess) return SPADE_ERR_DEVICE;
+  if (g_prof_start && g_prof_stop && hipEventRecord(g_prof_stop, s) != hipSuccess) return SPADE_ERR_DEVICE;
+  return SPADE_OK;
+}
+
 #define SPADE_TRY(expr)                       \
   do {                                        \
     const spade_status st_ = (expr);          \
@@ -252,11 +264,15 @@ spade_status spade_block_sparse_attn(const spade_problem* p, const void* q, cons
     void* kp = ws_ptr(workspace, L.kpack);
     void* vp = ws_ptr(workspace, L.vpack);
     SPADE_TRY(dev(launch_summarize(g, true, q, k, v, nullptr, nullptr, qp, kp, vp, s)));
-    return dev(launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o,
-                                  reinterpret_cast<int*>(ws_ptr(workspace, L.queue)), num_cus(), s));
+    return timed_attention(s, [&] {
+      return launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o,
+                                reinterpret_cast<int*>(ws_ptr(workspace, L.queue)), num_cus(), s);
+    });
   }
-  return dev(launch_bsattn_f32(g, (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
-                               col_capacity, scale, (float*)o, s));
+  return timed_attention(s, [&] {
+    return launch_bsattn_f32(g, (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
+                             col_capacity, scale, (float*)o, s);
+  });
 }
 
 spade_status spade_attn(const spade_problem* p, const void* q, const void* k, const void* v,
@@ -283,13 +299,22 @@ spade_status spade_attn(const spade_problem* p, const void* q, const void* k, co
     void* vp = ws_ptr(workspace, L.vpack);
     SPADE_TRY(dev(launch_summarize(g, true, q, k, v, qm, km, qp, kp, vp, s)));
     SPADE_TRY(run_select(p, g, L, qm, km, budget, row_ptr, col_idx, workspace, s));
-    return dev(launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o,
-                                  reinterpret_cast<int*>(ws_ptr(workspace, L.queue)), num_cus(), s));
+    return timed_attention(s, [&] {
+      return launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o,
+                                reinterpret_cast<int*>(ws_ptr(workspace, L.queue)), num_cus(), s);
+    });
   }
   SPADE_TRY(dev(launch_summarize(g, false, q, k, nullptr, qm, km, nullptr, nullptr, nullptr, s)));
   SPADE_TRY(run_select(p, g, L, qm, km, budget, row_ptr, col_idx, workspace, s));
-  return dev(launch_bsattn_f32(g, (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
-                               col_capacity, scale, (float*)o, s));
+  return timed_attention(s, [&] {
+    return launch_bsattn_f32(g, (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
+                             col_capacity, scale, (float*)o, s);
+  });
+}
+
+void spade_profile_events(void* start, void* stop) {
+  g_prof_start = (hipEvent_t)start;
+  g_prof_stop = (hipEvent_t)stop;
 }
 
 spade_status spade_debug_scores(const spade_problem* p, const float* q_mean, const float* k_mean,

@@ -23,7 +23,7 @@ OK, INVALID, UNSUP, CAP = (spade.SPADE_OK, spade.SPADE_ERR_INVALID_ARG, spade.SP
 def _declared_symbols():
     text = open(os.path.join(ROOT, "include", "spade.h")).read()
     return sorted(set(re.findall(
-        r"^(?:const\s+char\s*\*|int32_t|int64_t|size_t|spade_status)\s+(spade_\w+)\s*\(", text, re.M)))
+        r"^(?:const\s+char\s*\*|int32_t|int64_t|size_t|spade_status|void)\s+(spade_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
