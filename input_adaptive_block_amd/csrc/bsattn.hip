@@ -95,41 +95,50 @@ __global__ __launch_bounds__(kQThreads) void queue_kernel(int R, const int* __re
 // bf16 attention
 // ---------------------------------------------------------------------------
 
-template <int D>
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kListChunk = 4096;  // kept-block ids staged in LDS per pass
+
+// Position in a row's kept-block list: block j (entry pos of the staged list),
+// subtiles [s0, s0 + ns) of it, nk valid keys from subtile s0 on.
 struct Stage {
-  int kb;     // position in col_idx, or -1 when done
-  int j;      // KV block
-  int s0;     // first 32-key subtile of the stage
-  int ns;     // subtiles in the stage (1 or 2)
-  int nkeys;  // valid keys from subtile s0 on
+  int pos;  // -1: no more stages
+  int j;
+  int n;    // tokens of block j
+  int s0;
+  int ns;
+  int nk;
 };
 
-template <int D>
-__device__ inline Stage<D> find_stage(const Geom& g, const int* __restrict__ col_idx, int kb, int hi,
-                                      int s0) {
-  Stage<D> st;
-  while (kb < hi) {
-    const int j = col_idx[kb];
-    if (j >= 0 && j < g.nblk) {
-      const int n = block_box(g, j).n;
-      const int nsub = (n + 31) >> 5;
-      if (s0 < nsub) {
-        st.kb = kb;
-        st.j = j;
-        st.s0 = s0;
-        st.ns = min(2, nsub - s0);
-        st.nkeys = n - 32 * s0;
-        return st;
-      }
-    }
-    ++kb;
+__device__ inline Stage stage_at(const Geom& g, const uint16_t* list, int cn, int pos, int s0, int j, int n) {
+  Stage st;
+  for (;;) {
+    if (s0 > 0 && s0 < ((n + 31) >> 5)) break;  // more subtiles of the same block
     s0 = 0;
+    pos = pos + (j >= 0 ? 1 : 0);
+    j = -1;
+    while (pos < cn) {
+      const int jj = __builtin_amdgcn_readfirstlane((int)list[pos]);
+      if (jj < g.nblk) {
+        j = jj;
+        break;
+      }
+      ++pos;
+    }
+    if (j < 0) {
+      st.pos = -1;
+      st.j = 0; st.n = 0; st.s0 = 0; st.ns = 0; st.nk = 0;
+      return st;
+    }
+    n = block_box(g, j).n;
+    break;
   }
-  st.kb = -1;
-  st.j = 0;
-  st.s0 = 0;
-  st.ns = 0;
-  st.nkeys = 0;
+  st.pos = pos;
+  st.j = j;
+  st.n = n;
+  st.s0 = s0;
+  st.ns = min(2, ((n + 31) >> 5) - s0);
+  st.nk = n - 32 * s0;
   return st;
 }
 
@@ -139,10 +148,14 @@ __global__ __launch_bounds__(kThreads, 2) void bsattn_bf16_kernel(
     const uint16_t* __restrict__ vpack, const int* __restrict__ row_ptr, const int* __restrict__ col_idx,
     long long cap, float scale_log2, uint16_t* __restrict__ out, int* __restrict__ queue) {
   constexpr int SUB = 32 * D;          // bf16 elements of one 32-key subtile
+  constexpr int SUB_CPY = SUB * 2 / 1024;  // 1 KB wave copies per subtile
   constexpr int NC = D / 16;           // K-chunks of S^T
   constexpr int NM = D / 32;           // channel tiles of O^T
-  constexpr int VPT = (2 * SUB / 8) / kThreads;  // 16B vectors per thread per 2-subtile tensor
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][2 * SUB];  // [buf][K,V][2 subtiles]
+  // two stage buffers as distinct objects, so the compiler can tell the
+  // in-flight copy into one from the operand reads of the other
+  __shared__ __attribute__((aligned(1024))) uint16_t kvA[2][2 * SUB];  // [K,V][2 subtiles]
+  __shared__ __attribute__((aligned(1024))) uint16_t kvB[2][2 * SUB];
+  __shared__ uint16_t list[kListChunk];
   __shared__ int s_item;
 
   const int tid = threadIdx.x;
@@ -154,6 +167,19 @@ __global__ __launch_bounds__(kThreads, 2) void bsattn_bf16_kernel(
   int* qcursor = queue + kQueues + 1;
   int qx = blockIdx.x % kQueues;
   int visited = 0;
+
+  // asynchronous HBM -> LDS copy of a stage (K and V subtiles) into buffer b:
+  // each wave moves 1 KB per instruction, lane L's 16 bytes to offset 16 L
+  auto issue = [&](const Stage& st, uint16_t (&buf)[2][2 * SUB], size_t head_off) {
+    const size_t src = head_off + (size_t)st.j * g.P * D + (size_t)st.s0 * SUB;
+    const char* ks = reinterpret_cast<const char*>(kpack + src) + lane * 16;
+    const char* vs = reinterpret_cast<const char*>(vpack + src) + lane * 16;
+    const int ncpy = st.ns * SUB_CPY;
+    for (int t = wave; t < ncpy; t += kWaves) {
+      __builtin_amdgcn_global_load_lds(ks + t * 1024, (lds_void*)(&buf[0][t * 512]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vs + t * 1024, (lds_void*)(&buf[1][t * 512]), 16, 0, 0);
+    }
+  };
 
   for (;;) {
     if (tid == 0) {
@@ -172,7 +198,6 @@ __global__ __launch_bounds__(kThreads, 2) void bsattn_bf16_kernel(
     }
     __syncthreads();
     const int item = s_item;
-    __syncthreads();
     if (item < 0) break;
 
     const int row = item / nqt;
@@ -202,107 +227,109 @@ __global__ __launch_bounds__(kThreads, 2) void bsattn_bf16_kernel(
       for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
     float mref = -__builtin_huge_valf();
     float lsum = 0.f;
+    const size_t head_off = (size_t)bh * g.nblk * (size_t)g.P * D;
 
-    const size_t kv_head = (size_t)bh * g.nblk * (size_t)g.P * D;
-    Vec16 pre[2 * VPT];
-    auto issue = [&](const Stage<D>& st) {
-      const size_t base = kv_head + (size_t)st.j * g.P * D + (size_t)st.s0 * SUB;
-      const int nv = st.ns * (SUB / 8);
+    // one stage: S^T, online softmax and O^T update for each of its subtiles
+    auto compute = [&](const Stage& st_, uint16_t (&buf)[2][2 * SUB]) {
+        if (active) {
+          for (int st = 0; st < st_.ns; ++st) {
+            const bf16x8* kl = reinterpret_cast<const bf16x8*>(&buf[0][st * SUB]);
+            const bf16x8* vl = reinterpret_cast<const bf16x8*>(&buf[1][st * SUB]);
+            f32x16 s;
 #pragma unroll
-      for (int t = 0; t < VPT; ++t) {
-        const int vi = tid + t * kThreads;
-        if (vi < nv) {
-          pre[t] = *reinterpret_cast<const Vec16*>(kpack + base + (size_t)vi * 8);
-          pre[VPT + t] = *reinterpret_cast<const Vec16*>(vpack + base + (size_t)vi * 8);
-        }
-      }
-    };
-    auto store = [&](int b, const Stage<D>& st) {
-      const int nv = st.ns * (SUB / 8);
+            for (int v = 0; v < 16; ++v) s[v] = 0.f;
 #pragma unroll
-      for (int t = 0; t < VPT; ++t) {
-        const int vi = tid + t * kThreads;
-        if (vi < nv) {
-          *reinterpret_cast<Vec16*>(&lds[b][0][vi * 8]) = pre[t];
-          *reinterpret_cast<Vec16*>(&lds[b][1][vi * 8]) = pre[VPT + t];
-        }
-      }
-    };
-
-    Stage<D> cur = find_stage<D>(g, col_idx, (int)lo, (int)hi, 0);
-    if (cur.kb >= 0) {
-      issue(cur);
-      store(0, cur);
-    }
-    __syncthreads();
-    int b = 0;
-    while (cur.kb >= 0) {
-      Stage<D> nxt = find_stage<D>(g, col_idx, cur.kb, (int)hi, cur.s0 + cur.ns);
-      if (nxt.kb >= 0) issue(nxt);
-      if (active) {
-        for (int st = 0; st < cur.ns; ++st) {
-          const bf16x8* kl = reinterpret_cast<const bf16x8*>(&lds[b][0][st * SUB]);
-          const bf16x8* vl = reinterpret_cast<const bf16x8*>(&lds[b][1][st * SUB]);
-          f32x16 s;
+            for (int c = 0; c < NC; ++c)
+              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[c * 64 + lane], qop[c], s, 0, 0, 0);
+            const int kvalid = st_.nk - 32 * st;
+            if (kvalid < 32) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) s[v] = 0.f;
+              for (int v = 0; v < 16; ++v) {
+                const int key = 8 * (v >> 2) + 4 * half + (v & 3);
+                if (key >= kvalid) s[v] = -__builtin_huge_valf();
+              }
+            }
+            float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-          for (int c = 0; c < NC; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[c * 64 + lane], qop[c], s, 0, 0, 0);
-          const int kv = cur.nkeys - 32 * st;
-          if (kv < 32) {
+            for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, s[v]), s[v + 1]);
+            mx = fmaxf(mx, s[15]);
+            {
+              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+              mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            const float mnew = mx * scale_log2;
+            if (mnew > mref + kLazy) {
+              const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+              lsum *= alpha;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int key = 8 * (v >> 2) + 4 * half + (v & 3);
-              if (key >= kv) s[v] = -__builtin_huge_valf();
+              for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[m][v] *= alpha;
+              mref = mnew;
+            }
+            // p in bf16 (RNE); the row sum adds exactly those rounded values
+            // (v_dot2_f32_bf16 against ones), so the normalisation matches
+            // the weights the PV product uses
+            bf16x2 pr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e], scale_log2, -mref));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e + 1], scale_log2, -mref));
+              pr[e][0] = (__bf16)p0;
+              pr[e][1] = (__bf16)p1;
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
+            }
+            const bf16x8 pk0 = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                                       __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3),
+                                                       0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 pk1 = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
+                                                       __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3),
+                                                       0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+              acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl[(m * 2 + 0) * 64 + lane], pk0, acc[m], 0, 0, 0);
+              acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl[(m * 2 + 1) * 64 + lane], pk1, acc[m], 0, 0, 0);
             }
           }
-          float mx = s[0];
-#pragma unroll
-          for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float mnew = mx * scale_log2;
-          if (mnew > mref + kLazy) {
-            const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
-            lsum *= alpha;
-#pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) acc[m][v] *= alpha;
-            mref = mnew;
-          }
-          // p in bf16 (RNE); the row sum adds exactly those rounded values
-          // (v_dot2_f32_bf16 against ones), so the normalisation matches the
-          // weights the PV product uses
-          bf16x2 pr[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e], scale_log2, -mref));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e + 1], scale_log2, -mref));
-            pr[e][0] = (__bf16)p0;
-            pr[e][1] = (__bf16)p1;
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
-          }
-          const bf16x8 pk0 = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
-                                                     __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3),
-                                                     0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 pk1 = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
-                                                     __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3),
-                                                     0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl[(m * 2 + 0) * 64 + lane], pk0, acc[m], 0, 0, 0);
-            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl[(m * 2 + 1) * 64 + lane], pk1, acc[m], 0, 0, 0);
-          }
         }
+    };
+
+    for (long long c0 = lo; c0 < hi; c0 += kListChunk) {
+      const int cn = (int)min((long long)kListChunk, hi - c0);
+      __syncthreads();  // earlier readers of list / kv are done
+      for (int t = tid; t < cn; t += kThreads) {
+        const int j = col_idx[c0 + t];
+        list[t] = (j >= 0 && j < g.nblk) ? (uint16_t)j : (uint16_t)0xFFFF;
       }
-      if (nxt.kb >= 0) store(b ^ 1, nxt);
       __syncthreads();
-      cur = nxt;
-      b ^= 1;
+      Stage cur = stage_at(g, list, cn, 0, 0, -1, 0);
+      if (cur.pos < 0) continue;
+      issue(cur, kvA, head_off);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      // stages alternate between kvA and kvB; the copy of the next stage is
+      // in flight while this one is computed
+      for (;;) {
+        const Stage nxt = stage_at(g, list, cn, cur.pos, cur.s0 + cur.ns, cur.j, cur.n);
+        if (nxt.pos >= 0) issue(nxt, kvB, head_off);
+        compute(cur, kvA);
+        // the next stage's copy has landed for this wave; the barrier makes
+        // it (and the end of every read of the other buffer) visible to all
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (nxt.pos < 0) break;
+        cur = stage_at(g, list, cn, nxt.pos, nxt.s0 + nxt.ns, nxt.j, nxt.n);
+        if (cur.pos >= 0) issue(cur, kvA, head_off);
+        compute(nxt, kvB);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (cur.pos < 0) break;
+      }
     }
 
     if (active) {
-      const float ltot = lsum + __shfl_xor(lsum, 32);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+      const float ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
       const int qi = 32 * qsub + (lane & 31);
       if (qi < qbox.n) {
@@ -321,6 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsattn_bf16_kernel(
           }
       }
     }
+    __syncthreads();  // s_item and list are reused by the next item
   }
 }
 
