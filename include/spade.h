@@ -124,9 +124,10 @@ spade_status spade_estimate_select(const spade_problem* p, const float* q_mean, 
 /* Flash block-sparse attention ("Flash Block-Sparse Attention"): for every
  * query token of Q block i, softmax(scale * q K_sel^T) V_sel over all tokens of
  * the KV blocks listed in CSR row i, written to o [B, H, N, d] in Q's dtype.
- * Any CSR is accepted: ids outside [0, nblk), row extents outside
- * [0, col_capacity] or decreasing row_ptr are skipped (never read out of
- * bounds); a row with no valid block writes zeros. */
+ * A CSR row is a SET of blocks: ids may come in any order and a repeated id
+ * counts once.  Any CSR is accepted: ids outside [0, nblk), row extents
+ * outside [0, col_capacity] or decreasing row_ptr are skipped (never read out
+ * of bounds); a row with no valid block writes zeros. */
 spade_status spade_block_sparse_attn(const spade_problem* p, const void* q, const void* k, const void* v,
                                      const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
                                      void* o, void* workspace, size_t ws_bytes, void* stream);

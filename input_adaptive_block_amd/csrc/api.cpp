@@ -161,7 +161,9 @@ Workspace workspace_layout(const Geom& g) {
   L.scores = off; off = align256(off + (size_t)g.R * g.nblk * 8);
   L.qmean = off; off = align256(off + (size_t)g.BH * g.nblk * g.d * 4);
   L.kmean = off; off = align256(off + (size_t)g.BH * g.nblk * g.d * 4);
-  const size_t pack = g.bf16 ? (size_t)g.BH * g.nblk * g.P * g.d * 2 : 0;
+  // packed tiles plus two spare 32-row subtiles: the attention kernel copies
+  // whole two-subtile stages, which may run one subtile past a block's tile
+  const size_t pack = g.bf16 ? ((size_t)g.BH * g.nblk * g.P + 64) * g.d * 2 : 0;
   L.qpack = off; off = align256(off + pack);
   L.kpack = off; off = align256(off + pack);
   L.vpack = off; off = align256(off + pack);

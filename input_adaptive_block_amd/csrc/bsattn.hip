@@ -7,26 +7,32 @@
 // launch to raise occupancy ("Head Grouping").  The pages' kernel targets
 // Hopper (TMA, warp-group MMA); this one is written for CDNA4:
 //
-// * Work item = (selection row, 128-query tile).  One persistent grid pulls
-//   items from eight contiguous queues, one per XCD, whose row ranges hold
-//   equal shares of kept blocks; a workgroup starts on queue blockIdx % 8 (the
-//   XCD the dispatcher places it on) and steals from the next queues when its
-//   own is empty.  Neighbouring Q blocks of one head therefore run together on
-//   one XCD and share that XCD's L2 for the K/V blocks they both keep.
-// * 4 wavefronts x 32 queries.  Scores are computed transposed,
-//   S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane then owns one query
-//   and 16 keys, so the row max and row sum are in-lane (one cross-half
-//   exchange), and the S^T accumulator converted to bf16 is directly the B
-//   operand of O^T += V^T P^T.  Q operands stay in registers for the item.
-// * K and V come pre-packed (by the summarize kernel) in MFMA operand order,
-//   so each 32-key subtile is one contiguous 8 KB copy HBM -> LDS and every
-//   LDS operand read is a contiguous 1 KB ds_read_b128 per wavefront.  Stages
-//   of two subtiles are double-buffered in LDS (64 KB per workgroup, two
-//   workgroups per CU).
-// * fp32 online softmax in the exp2 domain with the log2(e) factor folded into
-//   the scale; the running max is only moved when a new score exceeds it by
-//   more than 2^8, which bounds every p by 256 (exact in value, fewer
-//   rescales of the 64-register O accumulator).
+// * Work unit = two consecutive (row, 128-query tile) items of one head --
+//   neighbouring Q blocks, whose kept KV sets overlap heavily.  The unit
+//   streams the UNION of their kept blocks once (ascending block id); each
+//   half of the workgroup (4 wavefronts x 32 queries) computes only on the
+//   blocks its own row keeps.  Every K/V byte fetched serves both tiles where
+//   they agree, which halves the L2 / Infinity-Cache traffic on video layers.
+// * One persistent workgroup of 8 wavefronts per CU pulls units from eight
+//   contiguous queues (one per XCD, equal shares of kept blocks); a workgroup
+//   starts on queue blockIdx % 8 and steals from the next queues when its own
+//   is empty, so neighbouring Q blocks of a head share one XCD's L2.
+// * Scores are computed transposed, S^T = K Q^T, with
+//   v_mfma_f32_32x32x16_bf16: each lane owns one query and 16 keys, so the row
+//   max and row sum are in-lane plus one permlane32 swap, and the S^T
+//   accumulator converted to bf16 is directly the B operand of
+//   O^T += V^T P^T.  Q operands stay in registers for the unit.
+// * K and V come pre-packed (by the summarize kernel) in MFMA operand order:
+//   a stage (two 32-key subtiles of K and of V, 32 KB at d = 128) is a
+//   contiguous HBM -> LDS copy issued with global_load_lds_dwordx4, and every
+//   LDS operand read is a contiguous 1 KB ds_read_b128 per wavefront (no bank
+//   conflicts).  Four stage buffers form a ring: three stages are in flight
+//   while one is computed.
+// * fp32 online softmax in the exp2 domain with log2(e) folded into the scale;
+//   the running max only moves when a score exceeds it by more than 2^8, which
+//   bounds every p by 256 (exact in value, fewer rescales of the 64-register O
+//   accumulator).  p is rounded to bf16 once and the row sum adds exactly the
+//   rounded values, so normalisation matches the weights PV used.
 #include "spade_internal.h"
 
 namespace spade {
@@ -35,38 +41,64 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWaves = 4;
+constexpr int kMembers = 2;                       // query tiles per work unit
+constexpr int kWavesPerMember = 4;                // 4 x 32 queries = one 128-query tile
+constexpr int kWaves = kMembers * kWavesPerMember;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQTile = 32 * kWaves;  // queries per work item
-constexpr float kLazy = 8.0f;        // log2 headroom before a rescale
+constexpr int kQTile = 32 * kWavesPerMember;
+constexpr float kLazy = 8.0f;                     // log2 headroom before a rescale
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-struct alignas(16) Vec16 {
-  uint32_t w[4];
+// Work units: the (row, q-tile) items of one head in order, two at a time.
+struct UnitMap {
+  int nqt;         // q-tiles per row
+  int items;       // items per head = nblk * nqt
+  int per_head;    // units per head = ceil(items / 2)
 };
 
+__host__ __device__ inline UnitMap unit_map(const Geom& g) {
+  UnitMap u;
+  u.nqt = (g.P + kQTile - 1) / kQTile;
+  u.items = g.nblk * u.nqt;
+  u.per_head = (u.items + kMembers - 1) / kMembers;
+  return u;
+}
+
 // ---------------------------------------------------------------------------
-// work queues: eight contiguous row ranges of equal cost (kept blocks + 1)
+// work queues: eight contiguous unit ranges of about equal cost
 // ---------------------------------------------------------------------------
 constexpr int kQThreads = 1024;
 
-__global__ __launch_bounds__(kQThreads) void queue_kernel(int R, const int* __restrict__ row_ptr,
+__device__ inline long long row_cost(const int* __restrict__ row_ptr, long long cap, int r) {
+  long long a = row_ptr[r], b = row_ptr[r + 1];
+  a = a < 0 ? 0 : (a > cap ? cap : a);
+  b = b < a ? a : (b > cap ? cap : b);
+  return b - a;
+}
+
+__global__ __launch_bounds__(kQThreads) void queue_kernel(Geom g, int U, const int* __restrict__ row_ptr,
                                                           long long cap, int* __restrict__ queue) {
   __shared__ long long part[kQThreads];
   __shared__ int start[kQueues + 1];
   const int tid = threadIdx.x;
-  if (tid <= kQueues) start[tid] = (tid == 0) ? 0 : R;
-  const int per = (R + kQThreads - 1) / kQThreads;
-  const int lo = min(R, tid * per), hi = min(R, lo + per);
-  auto cost = [&](int r) -> long long {
-    long long a = row_ptr[r], b = row_ptr[r + 1];
-    a = a < 0 ? 0 : (a > cap ? cap : a);
-    b = b < a ? a : (b > cap ? cap : b);
-    return b - a + 1;
+  const UnitMap um = unit_map(g);
+  if (tid <= kQueues) start[tid] = (tid == 0) ? 0 : U;
+  const int per = (U + kQThreads - 1) / kQThreads;
+  const int lo = min(U, tid * per), hi = min(U, lo + per);
+  // cost of a unit: kept blocks of its rows (a bound on its union) + 1
+  auto cost = [&](int u) -> long long {
+    const int bh = u / um.per_head, pi = u - bh * um.per_head;
+    long long c = 1;
+    for (int m = 0; m < kMembers; ++m) {
+      const int it = kMembers * pi + m;
+      if (it < um.items) c += row_cost(row_ptr, cap, bh * g.nblk + it / um.nqt);
+    }
+    return c;
   };
   long long s = 0;
-  for (int r = lo; r < hi; ++r) s += cost(r);
+  for (int u = lo; u < hi; ++u) s += cost(u);
   part[tid] = s;
   __syncthreads();
   for (int off = 1; off < kQThreads; off <<= 1) {
@@ -76,15 +108,16 @@ __global__ __launch_bounds__(kQThreads) void queue_kernel(int R, const int* __re
     __syncthreads();
   }
   const long long total = part[kQThreads - 1];
-  long long run = part[tid] - s;  // exclusive prefix before row lo
-  for (int r = lo; r < hi; ++r) {
-    const long long c = cost(r);
-    // start[x] = first row whose exclusive prefix reaches ceil(x * total / 8)
+  long long run = part[tid] - s;  // exclusive prefix before unit lo
+  long long prev = run;
+  for (int u = lo; u < hi; ++u) {
+    // start[x] = first unit whose exclusive prefix reaches ceil(x * total / 8)
     for (int x = 1; x < kQueues; ++x) {
       const long long t = (x * total + kQueues - 1) / kQueues;
-      if (run >= t && run - (r > 0 ? cost(r - 1) : 0) < t) start[x] = r;
+      if (run >= t && (u == 0 || prev < t)) start[x] = u;
     }
-    run += c;
+    prev = run;
+    run += cost(u);
   }
   __syncthreads();
   if (tid <= kQueues) queue[tid] = start[tid];
@@ -95,131 +128,173 @@ __global__ __launch_bounds__(kQThreads) void queue_kernel(int R, const int* __re
 // bf16 attention
 // ---------------------------------------------------------------------------
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int kListChunk = 4096;  // kept-block ids staged in LDS per pass
-
-// Position in a row's kept-block list: block j (entry pos of the staged list),
-// subtiles [s0, s0 + ns) of it, nk valid keys from subtile s0 on.
+// Position in the unit's union list: block j (entry pos), subtiles
+// [s0, s0 + ns) of it, nk valid keys from subtile s0 on, member bit mask.
 struct Stage {
-  int pos;  // -1: no more stages
+  int pos;  // -1: no stage
   int j;
-  int n;    // tokens of block j
+  int n;
   int s0;
   int ns;
   int nk;
+  int mask;
 };
 
-__device__ inline Stage stage_at(const Geom& g, const uint16_t* list, int cn, int pos, int s0, int j, int n) {
-  Stage st;
-  for (;;) {
-    if (s0 > 0 && s0 < ((n + 31) >> 5)) break;  // more subtiles of the same block
-    s0 = 0;
-    pos = pos + (j >= 0 ? 1 : 0);
-    j = -1;
-    while (pos < cn) {
-      const int jj = __builtin_amdgcn_readfirstlane((int)list[pos]);
-      if (jj < g.nblk) {
-        j = jj;
-        break;
-      }
-      ++pos;
-    }
-    if (j < 0) {
-      st.pos = -1;
-      st.j = 0; st.n = 0; st.s0 = 0; st.ns = 0; st.nk = 0;
+__device__ inline Stage next_stage(const Geom& g, const uint16_t* ul, int cnt, const Stage& cur) {
+  Stage st = cur;
+  if (cur.pos >= 0) {
+    const int nsub = (cur.n + 31) >> 5;
+    st.s0 = cur.s0 + cur.ns;
+    if (st.s0 < nsub) {
+      st.ns = min(2, nsub - st.s0);
+      st.nk = cur.n - 32 * st.s0;
       return st;
     }
-    n = block_box(g, j).n;
-    break;
   }
-  st.pos = pos;
-  st.j = j;
-  st.n = n;
-  st.s0 = s0;
-  st.ns = min(2, ((n + 31) >> 5) - s0);
-  st.nk = n - 32 * s0;
+  st.pos = cur.pos + 1;
+  if (st.pos >= cnt) {
+    st.pos = -1;
+    return st;
+  }
+  const int e = __builtin_amdgcn_readfirstlane((int)ul[st.pos]);
+  st.j = e & 0xFFF;
+  st.mask = e >> 12;
+  st.n = block_box(g, st.j).n;
+  st.s0 = 0;
+  st.ns = min(2, (st.n + 31) >> 5);
+  st.nk = st.n;
   return st;
 }
 
+// Wait until at most `stages` stages of this wave's copies (PER instructions
+// each) are still in flight.  s_waitcnt immediate on gfx9: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima (no wait).
+constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+template <int PER>
+__device__ inline void wait_copies(int stages) {
+  if (stages >= 2)
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * PER));
+  else if (stages == 1)
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(PER));
+  else
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bsattn_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     Geom g, const uint16_t* __restrict__ qpack, const uint16_t* __restrict__ kpack,
     const uint16_t* __restrict__ vpack, const int* __restrict__ row_ptr, const int* __restrict__ col_idx,
-    long long cap, float scale_log2, uint16_t* __restrict__ out, int* __restrict__ queue) {
-  constexpr int SUB = 32 * D;          // bf16 elements of one 32-key subtile
-  constexpr int SUB_CPY = SUB * 2 / 1024;  // 1 KB wave copies per subtile
-  constexpr int NC = D / 16;           // K-chunks of S^T
-  constexpr int NM = D / 32;           // channel tiles of O^T
-  // two stage buffers as distinct objects, so the compiler can tell the
-  // in-flight copy into one from the operand reads of the other
-  __shared__ __attribute__((aligned(1024))) uint16_t kvA[2][2 * SUB];  // [K,V][2 subtiles]
-  __shared__ __attribute__((aligned(1024))) uint16_t kvB[2][2 * SUB];
-  __shared__ uint16_t list[kListChunk];
-  __shared__ int s_item;
+    long long cap, float scale_log2, uint16_t* __restrict__ out, int* __restrict__ queue, int U) {
+  constexpr int SUB = 32 * D;                  // bf16 elements of one 32-key subtile
+  constexpr int STAGE_KB = 2 * SUB * 2 / 1024;  // 1 KB copies per tensor per stage (2 subtiles)
+  constexpr int CPW = STAGE_KB / kWaves;       // copies per wave per tensor
+  constexpr int PER = 2 * CPW;                 // copy instructions per wave per stage
+  constexpr int NC = D / 16;                   // K-chunks of S^T
+  constexpr int NM = D / 32;                   // channel tiles of O^T
+  static_assert(STAGE_KB % kWaves == 0, "stage copies split evenly over the waves");
+  // four stage buffers as distinct objects, so the compiler can tell the
+  // in-flight copies into three of them from the operand reads of the fourth
+  __shared__ __attribute__((aligned(1024))) uint16_t kv0[2][2 * SUB];  // [K,V][2 subtiles]
+  __shared__ __attribute__((aligned(1024))) uint16_t kv1[2][2 * SUB];
+  __shared__ __attribute__((aligned(1024))) uint16_t kv2[2][2 * SUB];
+  __shared__ __attribute__((aligned(1024))) uint16_t kv3[2][2 * SUB];
+  __shared__ uint8_t flags[kMembers][kMaxBlocks];
+  __shared__ uint16_t ulist[kMaxBlocks];
+  __shared__ int scanbuf[kThreads];
+  __shared__ int s_unit;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
-  const int nqt = (g.P + kQTile - 1) / kQTile;
+  const int member = wave / kWavesPerMember;
+  const int lw = wave - member * kWavesPerMember;
+  const UnitMap um = unit_map(g);
   const int* qstart = queue;
   int* qcursor = queue + kQueues + 1;
   int qx = blockIdx.x % kQueues;
   int visited = 0;
 
-  // asynchronous HBM -> LDS copy of a stage (K and V subtiles) into buffer b:
-  // each wave moves 1 KB per instruction, lane L's 16 bytes to offset 16 L
-  auto issue = [&](const Stage& st, uint16_t (&buf)[2][2 * SUB], size_t head_off) {
-    const size_t src = head_off + (size_t)st.j * g.P * D + (size_t)st.s0 * SUB;
-    const char* ks = reinterpret_cast<const char*>(kpack + src) + lane * 16;
-    const char* vs = reinterpret_cast<const char*>(vpack + src) + lane * 16;
-    const int ncpy = st.ns * SUB_CPY;
-    for (int t = wave; t < ncpy; t += kWaves) {
-      __builtin_amdgcn_global_load_lds(ks + t * 1024, (lds_void*)(&buf[0][t * 512]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vs + t * 1024, (lds_void*)(&buf[1][t * 512]), 16, 0, 0);
-    }
-  };
-
   for (;;) {
     if (tid == 0) {
-      int item = -1;
+      int unit = -1;
       while (visited < kQueues) {
-        const int n = (qstart[qx + 1] - qstart[qx]) * nqt;
+        const int n = qstart[qx + 1] - qstart[qx];
         const int it = n > 0 ? atomicAdd(&qcursor[qx], 1) : 0;
         if (it < n) {
-          item = qstart[qx] * nqt + it;
+          unit = qstart[qx] + it;
           break;
         }
         ++visited;
         qx = (qx + 1) % kQueues;
       }
-      s_item = item;
+      s_unit = unit;
     }
     __syncthreads();
-    const int item = s_item;
-    if (item < 0) break;
+    const int unit = s_unit;
+    if (unit < 0) break;
 
-    const int row = item / nqt;
-    const int qt = item - row * nqt;
-    const int bh = row / g.nblk;
-    const int i = row - bh * g.nblk;
-    const BlockBox qbox = block_box(g, i);
-    const int qsub = qt * kWaves + wave;
-    const bool active = 32 * qsub < qbox.n;
+    const int bh = unit / um.per_head;
+    const int pi = unit - bh * um.per_head;
+    const size_t head_off = (size_t)bh * g.nblk * (size_t)g.P * D;
 
-    // Q^T operands for this wave's 32 queries
+    // ---- the unit's union list of kept blocks, with member masks ----
+    for (int t = tid; t < g.nblk; t += kThreads) {
+      flags[0][t] = 0;
+      flags[1][t] = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kMembers; ++m) {
+      const int it = kMembers * pi + m;
+      if (it >= um.items) continue;
+      const int r = bh * g.nblk + it / um.nqt;
+      long long a = row_ptr[r], b = row_ptr[r + 1];
+      a = a < 0 ? 0 : (a > cap ? cap : a);
+      b = b < a ? a : (b > cap ? cap : b);
+      for (long long e = a + tid; e < b; e += kThreads) {
+        const int j = col_idx[e];
+        if (j >= 0 && j < g.nblk) flags[m][j] = 1;
+      }
+    }
+    __syncthreads();
+    const int per = (g.nblk + kThreads - 1) / kThreads;
+    const int jb = min(g.nblk, tid * per), je = min(g.nblk, jb + per);
+    int cnt = 0;
+    for (int j = jb; j < je; ++j) cnt += (flags[0][j] | flags[1][j]) != 0;
+    scanbuf[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int add = tid >= off ? scanbuf[tid - off] : 0;
+      __syncthreads();
+      scanbuf[tid] += add;
+      __syncthreads();
+    }
+    {
+      int w = scanbuf[tid] - cnt;
+      for (int j = jb; j < je; ++j) {
+        const int msk = flags[0][j] | (flags[1][j] << 1);
+        if (msk) ulist[w++] = (uint16_t)(j | (msk << 12));
+      }
+    }
+    const int ucnt = scanbuf[kThreads - 1];
+    __syncthreads();
+
+    // ---- this wave's 32 queries ----
+    const int my_it = kMembers * pi + member;
+    const bool has_item = my_it < um.items;
+    const int my_i = has_item ? my_it / um.nqt : 0;
+    const int my_qt = has_item ? my_it - my_i * um.nqt : 0;
+    const BlockBox qbox = block_box(g, my_i);
+    const int qsub = my_qt * kWavesPerMember + lw;
+    const bool active = has_item && 32 * qsub < qbox.n;
     bf16x8 qop[NC];
     if (active) {
-      const uint16_t* qp = qpack + ((size_t)bh * g.nblk + i) * (size_t)g.P * D + (size_t)qsub * SUB;
+      const uint16_t* qp = qpack + ((size_t)bh * g.nblk + my_i) * (size_t)g.P * D + (size_t)qsub * SUB;
 #pragma unroll
       for (int c = 0; c < NC; ++c) qop[c] = *reinterpret_cast<const bf16x8*>(qp + ((size_t)c * 64 + lane) * 8);
     }
-
-    long long lo = row_ptr[row], hi = row_ptr[row + 1];
-    lo = lo < 0 ? 0 : (lo > cap ? cap : lo);
-    hi = hi < lo ? lo : (hi > cap ? cap : hi);
-
     f32x16 acc[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -227,103 +302,118 @@ __global__ __launch_bounds__(kThreads, 2) void bsattn_bf16_kernel(
       for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
     float mref = -__builtin_huge_valf();
     float lsum = 0.f;
-    const size_t head_off = (size_t)bh * g.nblk * (size_t)g.P * D;
 
-    // one stage: S^T, online softmax and O^T update for each of its subtiles
-    auto compute = [&](const Stage& st_, uint16_t (&buf)[2][2 * SUB]) {
-        if (active) {
-          for (int st = 0; st < st_.ns; ++st) {
-            const bf16x8* kl = reinterpret_cast<const bf16x8*>(&buf[0][st * SUB]);
-            const bf16x8* vl = reinterpret_cast<const bf16x8*>(&buf[1][st * SUB]);
-            f32x16 s;
+    // asynchronous HBM -> LDS copy of a stage: always two subtiles (the pack
+    // buffers carry one spare subtile at their end), wave w copies KB
+    // w*CPW .. w*CPW+CPW-1 of K and of V; lane L's 16 bytes land at 16 L
+    auto issue = [&](const Stage& st, uint16_t (&buf)[2][2 * SUB]) {
+      const size_t src = head_off + (size_t)st.j * g.P * D + (size_t)st.s0 * SUB;
+      const char* ks = reinterpret_cast<const char*>(kpack + src) + lane * 16;
+      const char* vs = reinterpret_cast<const char*>(vpack + src) + lane * 16;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) s[v] = 0.f;
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[c * 64 + lane], qop[c], s, 0, 0, 0);
-            const int kvalid = st_.nk - 32 * st;
-            if (kvalid < 32) {
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int key = 8 * (v >> 2) + 4 * half + (v & 3);
-                if (key >= kvalid) s[v] = -__builtin_huge_valf();
-              }
-            }
-            float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-            for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, s[v]), s[v + 1]);
-            mx = fmaxf(mx, s[15]);
-            {
-              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-              mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            }
-            const float mnew = mx * scale_log2;
-            if (mnew > mref + kLazy) {
-              const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
-              lsum *= alpha;
-#pragma unroll
-              for (int m = 0; m < NM; ++m)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[m][v] *= alpha;
-              mref = mnew;
-            }
-            // p in bf16 (RNE); the row sum adds exactly those rounded values
-            // (v_dot2_f32_bf16 against ones), so the normalisation matches
-            // the weights the PV product uses
-            bf16x2 pr[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e], scale_log2, -mref));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e + 1], scale_log2, -mref));
-              pr[e][0] = (__bf16)p0;
-              pr[e][1] = (__bf16)p1;
-              lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
-            }
-            const bf16x8 pk0 = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
-                                                       __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3),
-                                                       0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 pk1 = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
-                                                       __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3),
-                                                       0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-              acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl[(m * 2 + 0) * 64 + lane], pk0, acc[m], 0, 0, 0);
-              acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl[(m * 2 + 1) * 64 + lane], pk1, acc[m], 0, 0, 0);
-            }
-          }
-        }
+      for (int c = 0; c < CPW; ++c) {
+        const int t = wave * CPW + c;
+        __builtin_amdgcn_global_load_lds(ks + t * 1024, (lds_void*)(&buf[0][t * 512]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vs + t * 1024, (lds_void*)(&buf[1][t * 512]), 16, 0, 0);
+      }
     };
 
-    for (long long c0 = lo; c0 < hi; c0 += kListChunk) {
-      const int cn = (int)min((long long)kListChunk, hi - c0);
-      __syncthreads();  // earlier readers of list / kv are done
-      for (int t = tid; t < cn; t += kThreads) {
-        const int j = col_idx[c0 + t];
-        list[t] = (j >= 0 && j < g.nblk) ? (uint16_t)j : (uint16_t)0xFFFF;
+    // one stage: S^T, online softmax and O^T update for each of its subtiles
+    auto compute = [&](const Stage& sg, uint16_t (&buf)[2][2 * SUB]) {
+      if (!active || !((sg.mask >> member) & 1)) return;
+      for (int st = 0; st < sg.ns; ++st) {
+        const bf16x8* kl = reinterpret_cast<const bf16x8*>(&buf[0][st * SUB]);
+        const bf16x8* vl = reinterpret_cast<const bf16x8*>(&buf[1][st * SUB]);
+        f32x16 s;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[c * 64 + lane], qop[c], s, 0, 0, 0);
+        const int kvalid = sg.nk - 32 * st;
+        if (kvalid < 32) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = 8 * (v >> 2) + 4 * half + (v & 3);
+            if (key >= kvalid) s[v] = -__builtin_huge_valf();
+          }
+        }
+        float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+        for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, s[v]), s[v + 1]);
+        mx = fmaxf(mx, s[15]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mnew = mx * scale_log2;
+        if (mnew > mref + kLazy) {
+          const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+          lsum *= alpha;
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[m][v] *= alpha;
+          mref = mnew;
+        }
+        bf16x2 pr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e], scale_log2, -mref));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e + 1], scale_log2, -mref));
+          pr[e][0] = (__bf16)p0;
+          pr[e][1] = (__bf16)p1;
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
+        }
+        const bf16x8 pk0 = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                                   __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 pk1 = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
+                                                   __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl[(m * 2 + 0) * 64 + lane], pk0, acc[m], 0, 0, 0);
+          acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl[(m * 2 + 1) * 64 + lane], pk1, acc[m], 0, 0, 0);
+        }
       }
-      __syncthreads();
-      Stage cur = stage_at(g, list, cn, 0, 0, -1, 0);
-      if (cur.pos < 0) continue;
-      issue(cur, kvA, head_off);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      // stages alternate between kvA and kvB; the copy of the next stage is
-      // in flight while this one is computed
+    };
+
+    // ---- stage ring: three stages in flight while one is computed ----
+    Stage none;
+    none.pos = -1; none.j = 0; none.n = 0; none.s0 = 0; none.ns = 0; none.nk = 0; none.mask = 0;
+    Stage cur = next_stage(g, ulist, ucnt, none);
+    if (cur.pos >= 0) {
+      Stage s1 = next_stage(g, ulist, ucnt, cur);
+      Stage s2 = s1.pos >= 0 ? next_stage(g, ulist, ucnt, s1) : none;
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // nothing older in flight
+      issue(cur, kv0);
+      if (s1.pos >= 0) issue(s1, kv1);
+      if (s2.pos >= 0) issue(s2, kv2);
+      wait_copies<PER>((s1.pos >= 0) + (s2.pos >= 0));
+      __builtin_amdgcn_s_barrier();
+      auto step = [&](uint16_t (&kvc)[2][2 * SUB], uint16_t (&kvi)[2][2 * SUB]) -> bool {
+        Stage s3 = none;
+        if (s2.pos >= 0) {
+          s3 = next_stage(g, ulist, ucnt, s2);
+          if (s3.pos >= 0) issue(s3, kvi);
+        }
+        compute(cur, kvc);
+        // stage s1 has landed for this wave (s2 and s3 may still be in
+        // flight); the barrier makes it visible to all waves and ends every
+        // read of kvc before it is refilled.  A bare s_barrier: the fence of
+        // __syncthreads would also drain the copies still in flight.
+        wait_copies<PER>((s2.pos >= 0) + (s3.pos >= 0));
+        __builtin_amdgcn_s_barrier();
+        cur = s1;
+        s1 = s2;
+        s2 = s3;
+        return cur.pos >= 0;
+      };
       for (;;) {
-        const Stage nxt = stage_at(g, list, cn, cur.pos, cur.s0 + cur.ns, cur.j, cur.n);
-        if (nxt.pos >= 0) issue(nxt, kvB, head_off);
-        compute(cur, kvA);
-        // the next stage's copy has landed for this wave; the barrier makes
-        // it (and the end of every read of the other buffer) visible to all
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (nxt.pos < 0) break;
-        cur = stage_at(g, list, cn, nxt.pos, nxt.s0 + nxt.ns, nxt.j, nxt.n);
-        if (cur.pos >= 0) issue(cur, kvA, head_off);
-        compute(nxt, kvB);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (cur.pos < 0) break;
+        if (!step(kv0, kv3)) break;
+        if (!step(kv1, kv0)) break;
+        if (!step(kv2, kv1)) break;
+        if (!step(kv3, kv2)) break;
       }
     }
 
@@ -348,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsattn_bf16_kernel(
           }
       }
     }
-    __syncthreads();  // s_item and list are reused by the next item
+    __syncthreads();  // s_unit, flags and ulist are reused by the next unit
   }
 }
 
@@ -365,6 +455,7 @@ __global__ __launch_bounds__(kF32Threads) void bsattn_f32_kernel(
     float* __restrict__ out) {
   __shared__ float ks[kF32Keys][D];
   __shared__ float vs[kF32Keys][D];
+  __shared__ uint8_t seen[kMaxBlocks];
   const int row = blockIdx.x;
   const int bh = row / g.nblk;
   const int i = row - bh * g.nblk;
@@ -384,9 +475,17 @@ __global__ __launch_bounds__(kF32Threads) void bsattn_f32_kernel(
   long long lo = row_ptr[row], hi = row_ptr[row + 1];
   lo = lo < 0 ? 0 : (lo > cap ? cap : lo);
   hi = hi < lo ? lo : (hi > cap ? cap : hi);
+  for (int t = threadIdx.x; t < g.nblk; t += kF32Threads) seen[t] = 0;
+  __syncthreads();
   for (long long kb = lo; kb < hi; ++kb) {
     const int j = col_idx[kb];
     if (j < 0 || j >= g.nblk) continue;
+    // a row is a set of blocks: a repeated id is skipped
+    const bool dup = seen[j] != 0;
+    __syncthreads();
+    if (threadIdx.x == 0) seen[j] = 1;
+    __syncthreads();
+    if (dup) continue;
     const BlockBox kbox = block_box(g, j);
     for (int base = 0; base < kbox.n; base += kF32Keys) {
       const int nk = min(kF32Keys, kbox.n - base);
@@ -434,22 +533,23 @@ hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpac
                               const int* row_ptr, const int* col_idx, long long col_capacity, float scale,
                               void* o, int* queue, int num_cus, hipStream_t s) {
   if (g.R == 0) return hipSuccess;
-  queue_kernel<<<1, kQThreads, 0, s>>>(g.R, row_ptr, col_capacity, queue);
+  const UnitMap um = unit_map(g);
+  const int U = g.BH * um.per_head;
+  queue_kernel<<<1, kQThreads, 0, s>>>(g, U, row_ptr, col_capacity, queue);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long items = (long long)g.R * ((g.P + kQTile - 1) / kQTile);
-  long long grid = (long long)num_cus * 2;
-  if (grid > items) grid = items;
+  int grid = num_cus;  // one 8-wave workgroup per CU (LDS-limited)
+  if (grid > U) grid = U;
   if (grid < 1) grid = 1;
   const float scale_log2 = scale * 1.4426950408889634f;
   if (g.d == 128)
-    bsattn_bf16_kernel<128><<<(unsigned)grid, kThreads, 0, s>>>(
+    bsattn_bf16_kernel<128><<<grid, kThreads, 0, s>>>(
         g, (const uint16_t*)qpack, (const uint16_t*)kpack, (const uint16_t*)vpack, row_ptr, col_idx,
-        col_capacity, scale_log2, (uint16_t*)o, queue);
+        col_capacity, scale_log2, (uint16_t*)o, queue, U);
   else
-    bsattn_bf16_kernel<64><<<(unsigned)grid, kThreads, 0, s>>>(
+    bsattn_bf16_kernel<64><<<grid, kThreads, 0, s>>>(
         g, (const uint16_t*)qpack, (const uint16_t*)kpack, (const uint16_t*)vpack, row_ptr, col_idx,
-        col_capacity, scale_log2, (uint16_t*)o, queue);
+        col_capacity, scale_log2, (uint16_t*)o, queue, U);
   return hipGetLastError();
 }
 

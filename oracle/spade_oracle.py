@@ -234,7 +234,7 @@ def attention_block_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, toks: List[
     q, k, v are [N, d] fp64 of that head; kept lists KV blocks.
     Returns o [n_i, d] (and the [n_i, n_keys] weights and key ids if asked).
     """
-    kept = list(kept)
+    kept = sorted(set(int(j) for j in kept))  # reading: a row's kept blocks form a set
     qi = q[toks[i]]
     if not kept:  # reading: a row that keeps no block attends to nothing -> zeros
         z = np.zeros((len(toks[i]), v.shape[1]))
