@@ -140,7 +140,8 @@ struct Stage {
   int mask;
 };
 
-__device__ inline Stage next_stage(const Geom& g, const uint16_t* ul, int cnt, const Stage& cur) {
+__device__ inline Stage next_stage(const Geom& g, const uint16_t* ul, const uint16_t* un, int cnt,
+                                  const Stage& cur) {
   Stage st = cur;
   if (cur.pos >= 0) {
     const int nsub = (cur.n + 31) >> 5;
@@ -159,7 +160,7 @@ __device__ inline Stage next_stage(const Geom& g, const uint16_t* ul, int cnt, c
   const int e = __builtin_amdgcn_readfirstlane((int)ul[st.pos]);
   st.j = e & 0xFFF;
   st.mask = e >> 12;
-  st.n = block_box(g, st.j).n;
+  st.n = __builtin_amdgcn_readfirstlane((int)un[st.pos]);
   st.s0 = 0;
   st.ns = min(2, (st.n + 31) >> 5);
   st.nk = st.n;
@@ -201,6 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t kv3[2][2 * SUB];
   __shared__ uint8_t flags[kMembers][kMaxBlocks];
   __shared__ uint16_t ulist[kMaxBlocks];
+  __shared__ uint16_t ublkn[kMaxBlocks];  // tokens of each union entry's block
   __shared__ int scanbuf[kThreads];
   __shared__ int s_unit;
 
@@ -275,7 +277,10 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
       int w = scanbuf[tid] - cnt;
       for (int j = jb; j < je; ++j) {
         const int msk = flags[0][j] | (flags[1][j] << 1);
-        if (msk) ulist[w++] = (uint16_t)(j | (msk << 12));
+        if (msk) {
+          ublkn[w] = (uint16_t)block_box(g, j).n;
+          ulist[w++] = (uint16_t)(j | (msk << 12));
+        }
       }
     }
     const int ucnt = scanbuf[kThreads - 1];
@@ -319,101 +324,122 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     };
 
     // one stage: S^T, online softmax and O^T update for each of its subtiles
+    // pieces of one subtile: operand reads + S^T, masked row max with the rare
+    // rescale, and exp + PV
+    auto qk = [&](const uint16_t* kb, const uint16_t* vb, f32x16& sc, bf16x8 (&vop)[2 * NM]) {
+      const bf16x8* kl = reinterpret_cast<const bf16x8*>(kb);
+      const bf16x8* vl = reinterpret_cast<const bf16x8*>(vb);
+      bf16x8 kop[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kop[c] = kl[c * 64 + lane];
+#pragma unroll
+      for (int c = 0; c < 2 * NM; ++c) vop[c] = vl[c * 64 + lane];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qop[c], sc, 0, 0, 0);
+    };
+    auto max_rescale = [&](f32x16& sc, int kvalid) {
+      if (kvalid < 32) {
+        const int kk = kvalid - 4 * half;  // key of element v: 8 (v/4) + 4 half + v%4
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (8 * (v >> 2) + (v & 3) >= kk) sc[v] = -__builtin_huge_valf();
+      }
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+      for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, sc[v]), sc[v + 1]);
+      mx = fmaxf(mx, sc[15]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const float mnew = mx * scale_log2;
+      if (mnew > mref + kLazy) {
+        const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+        lsum *= alpha;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[m][v] *= alpha;
+        mref = mnew;
+      }
+    };
+    auto expp = [&](const f32x16& sc, bf16x8& pk0, bf16x8& pk1) {
+      bf16x2 pr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * e], scale_log2, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * e + 1], scale_log2, -mref));
+        pr[e][0] = (__bf16)p0;
+        pr[e][1] = (__bf16)p1;
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
+      }
+      pk0 = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                    __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      pk1 = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
+                                    __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto pv = [&](const bf16x8 (&vop)[2 * NM], const bf16x8& pk0, const bf16x8& pk1) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m * 2 + 0], pk0, acc[m], 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m * 2 + 1], pk1, acc[m], 0, 0, 0);
+    };
+
+    // one stage of this wave's row.  With two subtiles, the second S^T is
+    // issued in the same basic block as the first exp (independent work the
+    // scheduler can interleave) and the first PV.
     auto compute = [&](const Stage& sg, uint16_t (&buf)[2][2 * SUB]) {
       if (!active || !((sg.mask >> member) & 1)) return;
-      for (int st = 0; st < sg.ns; ++st) {
-        const bf16x8* kl = reinterpret_cast<const bf16x8*>(&buf[0][st * SUB]);
-        const bf16x8* vl = reinterpret_cast<const bf16x8*>(&buf[1][st * SUB]);
-        f32x16 s;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[c * 64 + lane], qop[c], s, 0, 0, 0);
-        const int kvalid = sg.nk - 32 * st;
-        if (kvalid < 32) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = 8 * (v >> 2) + 4 * half + (v & 3);
-            if (key >= kvalid) s[v] = -__builtin_huge_valf();
-          }
-        }
-        float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-        for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, s[v]), s[v + 1]);
-        mx = fmaxf(mx, s[15]);
-        {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float mnew = mx * scale_log2;
-        if (mnew > mref + kLazy) {
-          const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
-          lsum *= alpha;
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[m][v] *= alpha;
-          mref = mnew;
-        }
-        bf16x2 pr[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e], scale_log2, -mref));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e + 1], scale_log2, -mref));
-          pr[e][0] = (__bf16)p0;
-          pr[e][1] = (__bf16)p1;
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
-        }
-        const bf16x8 pk0 = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
-                                                   __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3),
-                                                   0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 pk1 = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
-                                                   __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3),
-                                                   0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl[(m * 2 + 0) * 64 + lane], pk0, acc[m], 0, 0, 0);
-          acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl[(m * 2 + 1) * 64 + lane], pk1, acc[m], 0, 0, 0);
-        }
+      f32x16 s0;
+      bf16x8 v0[2 * NM];
+      qk(&buf[0][0], &buf[1][0], s0, v0);
+      max_rescale(s0, sg.nk);
+      bf16x8 p00, p01;
+      if (sg.ns == 2) {
+        f32x16 s1;
+        bf16x8 v1[2 * NM];
+        expp(s0, p00, p01);
+        qk(&buf[0][SUB], &buf[1][SUB], s1, v1);
+        pv(v0, p00, p01);
+        max_rescale(s1, sg.nk - 32);
+        bf16x8 p10, p11;
+        expp(s1, p10, p11);
+        pv(v1, p10, p11);
+      } else {
+        expp(s0, p00, p01);
+        pv(v0, p00, p01);
       }
     };
 
-    // ---- stage ring: three stages in flight while one is computed ----
+    // ---- two buffer pairs: one pair of stages is computed while the next
+    // pair is copied; one barrier per pair of stages ----
     Stage none;
     none.pos = -1; none.j = 0; none.n = 0; none.s0 = 0; none.ns = 0; none.nk = 0; none.mask = 0;
-    Stage cur = next_stage(g, ulist, ucnt, none);
+    Stage cur = next_stage(g, ulist, ublkn, ucnt, none);
     if (cur.pos >= 0) {
-      Stage s1 = next_stage(g, ulist, ucnt, cur);
-      Stage s2 = s1.pos >= 0 ? next_stage(g, ulist, ucnt, s1) : none;
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // nothing older in flight
+      Stage s1 = next_stage(g, ulist, ublkn, ucnt, cur);
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
       issue(cur, kv0);
       if (s1.pos >= 0) issue(s1, kv1);
-      if (s2.pos >= 0) issue(s2, kv2);
-      wait_copies<PER>((s1.pos >= 0) + (s2.pos >= 0));
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
       __builtin_amdgcn_s_barrier();
-      auto step = [&](uint16_t (&kvc)[2][2 * SUB], uint16_t (&kvi)[2][2 * SUB]) -> bool {
-        Stage s3 = none;
-        if (s2.pos >= 0) {
-          s3 = next_stage(g, ulist, ucnt, s2);
-          if (s3.pos >= 0) issue(s3, kvi);
-        }
-        compute(cur, kvc);
-        // stage s1 has landed for this wave (s2 and s3 may still be in
-        // flight); the barrier makes it visible to all waves and ends every
-        // read of kvc before it is refilled.  A bare s_barrier: the fence of
-        // __syncthreads would also drain the copies still in flight.
-        wait_copies<PER>((s2.pos >= 0) + (s3.pos >= 0));
+      auto superstep = [&](uint16_t (&ca)[2][2 * SUB], uint16_t (&cb)[2][2 * SUB], uint16_t (&na)[2][2 * SUB],
+                           uint16_t (&nb)[2][2 * SUB]) -> bool {
+        const Stage s2 = s1.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, s1) : none;
+        const Stage s3 = s2.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, s2) : none;
+        if (s2.pos >= 0) issue(s2, na);
+        if (s3.pos >= 0) issue(s3, nb);
+        compute(cur, ca);
+        if (s1.pos >= 0) compute(s1, cb);
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         __builtin_amdgcn_s_barrier();
-        cur = s1;
-        s1 = s2;
-        s2 = s3;
+        cur = s2;
+        s1 = s3;
         return cur.pos >= 0;
       };
       for (;;) {
-        if (!step(kv0, kv3)) break;
-        if (!step(kv1, kv0)) break;
-        if (!step(kv2, kv1)) break;
-        if (!step(kv3, kv2)) break;
+        if (!superstep(kv0, kv1, kv2, kv3)) break;
+        if (!superstep(kv2, kv3, kv0, kv1)) break;
       }
     }
 

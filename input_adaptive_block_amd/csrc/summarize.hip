@@ -144,6 +144,13 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
     }
   }
 
+  // the spare subtiles after the last packed tile are read (and masked to
+  // zero weight) by the attention kernel's two-subtile stages: keep them zero
+  if (PACK && role > 0 && j == g.nblk - 1 && bh == g.BH - 1) {
+    uint16_t* tail = (role == 1 ? kpack : vpack) + (size_t)g.BH * g.nblk * g.P * D;
+    for (int t = tid; t < 64 * D / 8; t += kThreads) *reinterpret_cast<Vec16*>(tail + (size_t)t * 8) = Vec16{{0u, 0u, 0u, 0u}};
+  }
+
   if (!want_mean) return;
   // reduce over token slots: lanes with equal tid % TPT inside the wave ...
 #pragma unroll
