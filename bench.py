@@ -141,6 +141,9 @@ def main():
     ap.add_argument("--ratio", type=float, default=None, help="override the budget with a keep ratio")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the timed region, run a plain device copy of MIB MiB (a reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the heads shard across GPUs "
@@ -279,6 +282,14 @@ def main():
         "context": ("the pages report 2.26x-3.40x attention speedup over FlashAttention-3 on an NVIDIA "
                     "H800 for 720p video models; no absolute figure exists to compare with"),
     }
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = n * 4
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
