@@ -22,6 +22,9 @@ pages are silent (each also listed in the design notes):
   j = (it*nH + ih)*nW + iw; Q and KV use the same tiling;
 * the Summarizer is the mean over the block's real tokens, computed exactly
   and stored as fp32 (the summary tensor's storage type);
+* the intra-block estimate (SICS) of a block is the mean cosine similarity
+  over all ordered pairs of its real tokens, diagonal included (zero tokens:
+  cosine 0), so it lies in [0, 1];
 * the inter-block Estimator is S_ij = scale * <qbar_i, kbar_j>, scale = 1/sqrt(d);
 * selection orders blocks by (S descending, j ascending); a count or ratio
   budget keeps the first k (k = ceil(r*nK - 1e-6) clamped to [1, nK] for a
@@ -126,6 +129,43 @@ def summarize(x: np.ndarray, g: Geometry, store_f32: bool = True) -> np.ndarray:
     out = np.empty((B, H, len(toks), d), dtype=np.float64)
     for j, tk in enumerate(toks):
         out[:, :, j, :] = x[:, :, tk, :].sum(axis=2) / float(len(tk))
+    if store_f32:
+        out = out.astype(np.float32).astype(np.float64)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Intra-block estimator: Sum of Intra-block Cosine Similarities (SICS)
+# ---------------------------------------------------------------------------
+
+def sics(x: np.ndarray, g: Geometry, store_f32: bool = True) -> np.ndarray:
+    """Normalised SICS of every block of x [B, H, N, d] -> [B, H, nblk].
+
+    Technical summary, "Methodology 2. Scheme Generation", Aggregation
+    Evaluation: SICS sums the cosine similarities of the embeddings inside a
+    block; a high value means the block's tokens are tightly clustered.  Here
+    the sum runs over all ordered pairs (i, j) of the block's real tokens, the
+    pairs i = j included, and is divided by n_b^2, so it lies in [0, 1].  A
+    zero token has no direction: its cosine with anything is taken as 0 (it
+    still counts in n_b).
+
+    This is the plain O(n_b^2 d) definition, written as the sum of all
+    entries of U U^T where the rows of U are the block's unit token vectors;
+    the online form of the same page (Online Optimization, O(n_b d)) must
+    reach this value up to rounding.  fp64; with store_f32 the result is
+    rounded once to fp32.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, H, N, d = x.shape
+    assert N == g.N
+    toks = block_tokens(g)
+    out = np.empty((B, H, len(toks)), dtype=np.float64)
+    for j, tk in enumerate(toks):
+        xb = x[:, :, tk, :]                                   # [B, H, n, d]
+        norm = np.sqrt((xb * xb).sum(axis=-1, keepdims=True))
+        u = np.divide(xb, norm, out=np.zeros_like(xb), where=norm > 0)
+        cos = u @ np.swapaxes(u, -1, -2)                      # [B, H, n, n]
+        out[:, :, j] = cos.sum(axis=(-1, -2)) / float(len(tk)) ** 2
     if store_f32:
         out = out.astype(np.float32).astype(np.float64)
     return out

@@ -427,6 +427,83 @@ def test_single_block_is_dense_within_that_block():
 
 
 # ---------------------------------------------------------------------------
+# intra-block estimate (SICS: Sum of Intra-block Cosine Similarities)
+# ---------------------------------------------------------------------------
+
+def _sics_pairs(xb):
+    """Brute force over the ordered token pairs of one block, one cosine at a
+    time with math.fsum (zero tokens: cosine 0), divided by n^2."""
+    n = xb.shape[0]
+    norms = [math.sqrt(math.fsum(float(v) * float(v) for v in row)) for row in xb]
+    terms = []
+    for i in range(n):
+        for j in range(n):
+            if norms[i] == 0.0 or norms[j] == 0.0:
+                continue
+            terms.append(math.fsum(float(a) * float(b) for a, b in zip(xb[i], xb[j])) / (norms[i] * norms[j]))
+    return math.fsum(terms) / (n * n)
+
+
+def test_sics_equals_pairwise_bruteforce_on_ragged_blocks():
+    g = Geometry(3, 5, 4, 2, 2, 3)  # partial blocks along every axis
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 2, g.N, 6))
+    x[0, 1, 5] = 0.0  # a zero token
+    got = oracle.sics(x, g, store_f32=False)
+    for j, tk in enumerate(oracle.block_tokens(g)):
+        for h in range(2):
+            assert abs(got[0, h, j] - _sics_pairs(x[0, h, tk])) < 1e-13
+
+
+def test_sics_online_identity_is_exact():
+    """sum_{i,j} <u_i, u_j> = |sum_i u_i|^2 (bilinearity): the O(n d) online
+    form of the page reaches the pairwise definition up to rounding."""
+    cfg, g, x = _inputs("ragged_small")
+    got = oracle.sics(x["k"], g, store_f32=False)
+    xk = x["k"]
+    norm = np.sqrt((xk * xk).sum(-1, keepdims=True))
+    u = np.divide(xk, norm, out=np.zeros_like(xk), where=norm > 0)
+    for j, tk in enumerate(oracle.block_tokens(g)):
+        s = u[:, :, tk, :].sum(axis=2)
+        np.testing.assert_allclose(got[:, :, j], (s * s).sum(-1) / len(tk) ** 2, rtol=1e-12, atol=1e-15)
+
+
+def test_sics_closed_forms():
+    g = Geometry(1, 1, 4, 1, 1, 4)  # one block of 4 tokens
+    d = 5
+    v = np.array([1.0, -2.0, 0.5, 3.0, 0.25])
+    same = np.tile(v, (4, 1))[None, None]
+    assert oracle.sics(same, g, store_f32=False)[0, 0, 0] == pytest.approx(1.0, abs=1e-15)
+    # a token and its negation, twice: the unit vectors cancel
+    opp = np.stack([v, -v, 2 * v, -0.5 * v])[None, None]
+    assert abs(oracle.sics(opp, g, store_f32=False)[0, 0, 0]) < 1e-15
+    # orthonormal tokens: only the diagonal survives -> n / n^2
+    eye = np.eye(d)[:4][None, None] * np.array([1.0, 3.0, 0.2, 7.0])[:, None]
+    assert oracle.sics(eye, g, store_f32=False)[0, 0, 0] == pytest.approx(0.25, abs=1e-15)
+    # one live token, three zero tokens: |u|^2 / n^2
+    one = np.zeros((1, 1, 4, d))
+    one[0, 0, 2] = v
+    assert oracle.sics(one, g, store_f32=False)[0, 0, 0] == pytest.approx(1.0 / 16, abs=1e-15)
+    # two tokens at angle theta: (2 + 2 cos theta) / 4
+    g2 = Geometry(1, 1, 2, 1, 1, 2)
+    for theta in (0.3, 1.2, 2.9):
+        two = np.array([[1.0, 0.0], [math.cos(theta), math.sin(theta)]])[None, None]
+        assert oracle.sics(two, g2, store_f32=False)[0, 0, 0] == pytest.approx((2 + 2 * math.cos(theta)) / 4, abs=1e-15)
+
+
+def test_sics_invariant_to_token_scaling_and_rotation():
+    cfg, g, x = _inputs("ragged_p64")
+    q = x["q"][:, :1]
+    base = oracle.sics(q, g, store_f32=False)
+    rng = np.random.default_rng(3)
+    scaled = q * rng.uniform(0.1, 10.0, size=q.shape[:-1] + (1,))
+    np.testing.assert_allclose(oracle.sics(scaled, g, store_f32=False), base, rtol=1e-12, atol=1e-14)
+    rot, _ = np.linalg.qr(rng.standard_normal((cfg.d, cfg.d)))
+    np.testing.assert_allclose(oracle.sics(q @ rot, g, store_f32=False), base, rtol=1e-11, atol=1e-13)
+    assert (base >= -1e-15).all() and (base <= 1 + 1e-12).all()
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by one of the pins above
 # ---------------------------------------------------------------------------
 
@@ -476,3 +553,26 @@ def test_planted_mass_over_kept_only_is_caught():
     p /= p.sum()
     assert p[sel.row(0)].sum() >= 0.9 - 1e-15
     assert p[sel.row(0)[:-1]].sum() < 0.9
+
+
+def test_planted_sics_without_diagonal_is_caught():
+    """Dropping the i = j pairs (normalising by n(n-1)) fails the
+    orthonormal-tokens closed form (it gives 0 instead of 1/n)."""
+    eye = np.eye(4)[None, None]
+    n = 4
+    u = eye[0, 0]
+    bad = (u @ u.T - np.diag(np.diag(u @ u.T))).sum() / (n * (n - 1))
+    assert abs(bad - 0.25) > 0.2
+
+
+def test_planted_sics_dot_products_instead_of_cosines_is_caught():
+    """Summing raw dot products (no normalisation) breaks scale invariance."""
+    cfg, g, x = _inputs("tiny")
+    q = x["q"][:, :1]
+    toks = oracle.block_tokens(g)
+
+    def bad(y):
+        return np.array([(y[0, 0, tk] @ y[0, 0, tk].T).sum() / len(tk) ** 2 for tk in toks])
+
+    assert np.abs(bad(3.0 * q) - bad(q)).max() > 1e-3
+
