@@ -231,6 +231,9 @@ def main():
     ci2 = torch.empty_like(ci)
     o2 = torch.empty_like(o)
     summ_ms = timed(lambda: spade.spade_summarize(p, q, k, qm, km, stream))
+    qs = torch.empty(cfg.B, cfg.H, nblk, dtype=torch.float32, device=dev)
+    ks = torch.empty_like(qs)
+    sics_ms = timed(lambda: spade.spade_summarize_sics(p, q, k, qm, km, qs, ks, stream))
     sel_ms = timed(lambda: spade.spade_estimate_select(p, qm, km, bud, rp2, ci2, cap, ws, ws.numel(), stream))
     bsa_ms = timed(lambda: spade.spade_block_sparse_attn(p, q, k, v, rp, ci, cap, o2, ws, ws.numel(), stream))
     summ_bytes = 2 * q.numel() * q.element_size() + 2 * qm.numel() * 4
@@ -264,6 +267,8 @@ def main():
         "stages_ms": {
             "summarize": summ_ms,
             "summarize_GBps": summ_bytes / (summ_ms * 1e-3) / 1e9,
+            "summarize_with_sics": sics_ms,
+            "summarize_with_sics_GBps": (summ_bytes + 2 * qs.numel() * 4) / (sics_ms * 1e-3) / 1e9,
             "estimate_select": sel_ms,
             "block_sparse_attn_call": bsa_ms,
             "attention_kernel": attn_avg,

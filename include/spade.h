@@ -112,6 +112,23 @@ const char* spade_status_string(spade_status s);
 spade_status spade_summarize(const spade_problem* p, const void* q, const void* k,
                              float* q_mean, float* k_mean, void* stream);
 
+/* Summarizer plus the intra-block estimate of the same pass ("Methodology 2.
+ * Scheme Generation": Aggregation Evaluation and Online Optimization; fused
+ * with blocking and summarization as in "Kernel Fusion").  Writes the block
+ * means exactly as spade_summarize, and for each block the normalised Sum of
+ * Intra-block Cosine Similarities
+ *     q_sics[b,h,j] = sum over ordered token pairs (i, i') of block j of
+ *                     cos(q_i, q_i'), diagonal included, divided by n_j^2,
+ * a value in [0, 1] (a zero token has cosine 0 with everything and counts in
+ * n_j); likewise k_sics.  Computed in one read of the block with the online
+ * identity sum cos = |sum_i q_i/|q_i| |^2 in fp64, rounded once to fp32.
+ * q_sics, k_sics: fp32 [B, H, nblk]; either may be NULL (not computed).
+ * q, k, q_mean, k_mean must not be NULL (SPADE_ERR_INVALID_ARG, nothing is
+ * launched). */
+spade_status spade_summarize_sics(const spade_problem* p, const void* q, const void* k,
+                                  float* q_mean, float* k_mean, float* q_sics, float* k_sics,
+                                  void* stream);
+
 /* Estimator + index search: S_ij = scale * <q_mean_i, k_mean_j> in fp64, then
  * per row the blocks in (S descending, j ascending) order are kept by the
  * budget.  Writes row_ptr [R+1] and col_idx (ascending ids per row).

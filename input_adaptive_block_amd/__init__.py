@@ -14,15 +14,16 @@ from ._lib import (  # noqa: F401
     SPADE_KEEP_COUNT, SPADE_KEEP_MASS, SPADE_KEEP_RATIO, SPADE_OK, SPADE_ERR_CAPACITY,
     SPADE_ERR_DEVICE, SPADE_ERR_INVALID_ARG, SPADE_ERR_UNSUPPORTED, lib, spade_attn,
     spade_block_sparse_attn, spade_check, spade_debug_scores, spade_estimate_select,
-    spade_max_nnz, spade_num_blocks, spade_profile_events, spade_summarize, spade_workspace_bytes,
+    spade_max_nnz, spade_num_blocks, spade_profile_events, spade_summarize, spade_summarize_sics,
+    spade_workspace_bytes,
     status_string,
 )
 
 __all__ = [
-    "Problem", "Budget", "SpadeError", "problem_for", "summarize", "estimate_select",
+    "Problem", "Budget", "SpadeError", "problem_for", "summarize", "summarize_sics", "estimate_select",
     "block_sparse_attn", "attn", "debug_scores", "alloc_workspace",
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
-    "spade_summarize", "spade_estimate_select", "spade_block_sparse_attn", "spade_attn",
+    "spade_summarize", "spade_summarize_sics", "spade_estimate_select", "spade_block_sparse_attn", "spade_attn",
     "spade_debug_scores",
 ]
 
@@ -79,6 +80,24 @@ def summarize(q, k, grid, block) -> Tuple["object", "object"]:
     km = torch.empty_like(qm)
     spade_summarize(p, q, k, qm, km)
     return qm, km
+
+
+def summarize_sics(q, k, grid, block):
+    """Block means and the per-block intra-block cosine similarity (SICS, in
+    [0, 1]) of q and k: returns (q_mean, k_mean, q_sics, k_sics)."""
+    torch = _torch()
+    p = problem_for(q, grid, block)
+    nblk = spade_num_blocks(p)
+    if nblk < 0:
+        raise SpadeError(spade_check(p), "summarize_sics")
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", q.shape, q.dtype)
+    qm = torch.empty(p.B, p.H, nblk, p.d, dtype=torch.float32, device=q.device)
+    km = torch.empty_like(qm)
+    qs = torch.empty(p.B, p.H, nblk, dtype=torch.float32, device=q.device)
+    ks = torch.empty_like(qs)
+    spade_summarize_sics(p, q, k, qm, km, qs, ks)
+    return qm, km, qs, ks
 
 
 def estimate_select(q_mean, k_mean, problem: Problem, mode, per_head: Sequence[float], workspace=None):

@@ -104,6 +104,7 @@ def _load() -> ctypes.CDLL:
         "spade_check": (st, [P, Bp, i64]),
         "spade_status_string": (ctypes.c_char_p, [st]),
         "spade_summarize": (st, [P, vp, vp, vp, vp, vp]),
+        "spade_summarize_sics": (st, [P, vp, vp, vp, vp, vp, vp, vp]),
         "spade_estimate_select": (st, [P, vp, vp, Bp, vp, vp, i64, vp, sz, vp]),
         "spade_block_sparse_attn": (st, [P, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
         "spade_attn": (st, [P, vp, vp, vp, Bp, vp, vp, vp, i64, vp, sz, vp]),
@@ -121,7 +122,7 @@ _LIB = _load()
 
 EXPORTED = (
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
-    "spade_status_string", "spade_summarize", "spade_estimate_select",
+    "spade_status_string", "spade_summarize", "spade_summarize_sics", "spade_estimate_select",
     "spade_block_sparse_attn", "spade_attn", "spade_debug_scores", "spade_profile_events",
 )
 
@@ -180,6 +181,11 @@ def spade_check(problem: Problem, budget: Optional[Budget] = None, col_capacity:
 def spade_summarize(problem: Problem, q, k, q_mean, k_mean, stream=None) -> None:
     _check(_LIB.spade_summarize(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(q_mean), _ptr(k_mean),
                                 _stream(stream)), "spade_summarize")
+
+
+def spade_summarize_sics(problem: Problem, q, k, q_mean, k_mean, q_sics, k_sics, stream=None) -> None:
+    _check(_LIB.spade_summarize_sics(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(q_mean), _ptr(k_mean),
+                                     _ptr(q_sics), _ptr(k_sics), _stream(stream)), "spade_summarize_sics")
 
 
 def spade_estimate_select(problem: Problem, q_mean, k_mean, budget: Budget, row_ptr, col_idx,

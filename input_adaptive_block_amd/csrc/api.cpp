@@ -230,6 +230,16 @@ spade_status spade_summarize(const spade_problem* p, const void* q, const void* 
                               nullptr, (hipStream_t)stream));
 }
 
+spade_status spade_summarize_sics(const spade_problem* p, const void* q, const void* k, float* q_mean,
+                                  float* k_mean, float* q_sics, float* k_sics, void* stream) {
+  Geom g;
+  SPADE_TRY(make_geom(p, &g));
+  if (g.BH == 0) return SPADE_OK;
+  if (!q || !k || !q_mean || !k_mean) return SPADE_ERR_INVALID_ARG;
+  return dev(launch_summarize_sics(g, p->dtype == SPADE_BF16, q, k, q_mean, k_mean, q_sics, k_sics,
+                                   (hipStream_t)stream));
+}
+
 spade_status spade_estimate_select(const spade_problem* p, const float* q_mean, const float* k_mean,
                                    const spade_budget* budget, int32_t* row_ptr, int32_t* col_idx,
                                    int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream) {

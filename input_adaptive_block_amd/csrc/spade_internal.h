@@ -85,6 +85,10 @@ Workspace workspace_layout(const Geom& g);
 hipError_t launch_summarize(const Geom& g, bool bf16, const void* q, const void* k, const void* v,
                             float* q_mean, float* k_mean, void* qpack, void* kpack, void* vpack,
                             hipStream_t s);
+// block means plus the normalised intra-block cosine similarity (either sics
+// pointer may be null)
+hipError_t launch_summarize_sics(const Geom& g, bool bf16, const void* q, const void* k, float* q_mean,
+                                 float* k_mean, float* q_sics, float* k_sics, hipStream_t s);
 hipError_t launch_scores(const Geom& g, const float* q_mean, const float* k_mean, double scale,
                          double* scores, hipStream_t s);
 hipError_t launch_select(const Geom& g, const double* scores, const SelectArgs& a, int* counts,

@@ -6,6 +6,15 @@
 // ("Methodology 1. vDiT-SSR", Summarizer & Estimator Expressions): the mean of
 // a block's real tokens.
 //
+// Intra-block estimate (optional side output): SICS, the sum of intra-block
+// cosine similarities ("Methodology 2. Scheme Generation", Aggregation
+// Evaluation), normalised by n_b^2.  The online form (Online Optimization)
+// follows from bilinearity: with u_i = x_i / |x_i| (0 for a zero token),
+// sum_{i,j in b} cos(x_i, x_j) = |sum_i u_i|^2, so it rides on the same single
+// read of the block as the mean: each token's 16 threads reduce its squared
+// norm with shuffles, scale their 8 channels by 1/|x| and add them to a
+// second fp64 accumulator.
+//
 // One workgroup of 256 threads per (block j, head bh, role) with role
 // 0 = Q, 1 = K, 2 = V.  Each thread moves 16-byte vectors of one token: the
 // load of token l is a contiguous 16 B of its d-row, so a wave reads whole
@@ -33,19 +42,49 @@ struct alignas(16) Vec16 {
   uint32_t w[4];
 };
 
+// One DPP move of both halves of a double (CTRL is a DPP control code).
+template <int CTRL>
+__device__ inline double dpp_f64(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum of x over aligned groups of G consecutive lanes (G = 8, 16 or 32),
+// every lane of a group receiving the total.  Within a 16-lane row the
+// partners come from DPP (swap neighbours, swap pairs, mirror each half-row,
+// mirror the row), which pair disjoint partial sums at every step; across the
+// two rows of a 32-lane group one cross-lane shuffle finishes.
+template <int G>
+__device__ inline double group_sum(double x) {
+  constexpr int kSwap1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+  constexpr int kSwap2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+  constexpr int kHalfMirror = 0x141;  // row_half_mirror
+  constexpr int kMirror = 0x140;      // row_mirror
+  x += dpp_f64<kSwap1>(x);
+  x += dpp_f64<kSwap2>(x);
+  x += dpp_f64<kHalfMirror>(x);
+  if (G >= 16) x += dpp_f64<kMirror>(x);
+  if (G >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
 __device__ inline float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ inline float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-template <bool BF16, int D, bool PACK>
+template <bool BF16, int D, bool PACK, bool SICS>
 __global__ __launch_bounds__(kThreads) void summarize_kernel(
     Geom g, const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     float* __restrict__ q_mean, float* __restrict__ k_mean, uint16_t* __restrict__ qpack,
-    uint16_t* __restrict__ kpack, uint16_t* __restrict__ vpack) {
+    uint16_t* __restrict__ kpack, uint16_t* __restrict__ vpack, float* __restrict__ q_sics,
+    float* __restrict__ k_sics) {
   constexpr int EPV = BF16 ? 8 : 4;     // elements per 16-byte vector
   constexpr int TPT = D / EPV;          // threads per token row
   constexpr int TPP = kThreads / TPT;   // tokens per pass
   constexpr int VROW = D + 8;           // LDS row stride (bf16) of the V transpose
   static_assert(kThreads % TPT == 0, "layout");
+  static_assert(TPT == 8 || TPT == 16 || TPT == 32, "token lane groups");
 
   const int j = blockIdx.x;
   const int bh = blockIdx.y;
@@ -65,13 +104,20 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
 
   float* mean_out = role == 0 ? q_mean : (role == 1 ? k_mean : nullptr);
   const bool want_mean = mean_out != nullptr;
+  float* sics_out = SICS ? (role == 0 ? q_sics : (role == 1 ? k_sics : nullptr)) : nullptr;
+  const bool want_sics = SICS && sics_out != nullptr;
 
   __shared__ double red[kThreads / 64][D];
+  __shared__ double ured[SICS ? kThreads / 64 : 1][SICS ? D : 1];
   __shared__ uint16_t vt[PACK ? 128 * VROW : 1];
 
   double acc[EPV];
+  double uacc[EPV];  // sum of the unit token vectors (SICS)
 #pragma unroll
-  for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+  for (int e = 0; e < EPV; ++e) {
+    acc[e] = 0.0;
+    uacc[e] = 0.0;
+  }
 
   if (role < 2 || !PACK) {
     uint16_t* pk = nullptr;
@@ -82,17 +128,37 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
       if (l < box.n) {
         const int tok = block_token(g, box, l);
         x = *reinterpret_cast<const Vec16*>(src + (head_base + (size_t)tok * D + c0) * elem);
-        if (want_mean) {
-          if (BF16) {
+      }
+      if (want_mean || want_sics) {
+        double xe[EPV];
+        if (BF16) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              acc[2 * e] += (double)bf16_lo(x.w[e]);
-              acc[2 * e + 1] += (double)bf16_hi(x.w[e]);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(x.w[e]);
+          for (int e = 0; e < 4; ++e) {
+            xe[2 * e] = (double)bf16_lo(x.w[e]);
+            xe[2 * e + 1] = (double)bf16_hi(x.w[e]);
           }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xe[e] = (double)__uint_as_float(x.w[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] += xe[e];
+        if (want_sics) {
+          // squared norm of the token over its TPT threads (consecutive lanes;
+          // every thread of the group runs the same iterations)
+          double ss = 0.0;
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) ss += xe[e] * xe[e];
+          ss = group_sum<TPT>(ss);
+          // 1/|x|: fp32 reciprocal square root refined by one Newton step in
+          // fp64 (relative error ~1e-14, far below the fp32 result's ulp)
+          double inv = 0.0;
+          if (ss > 0.0) {
+            const double r = (double)__builtin_amdgcn_rsqf((float)ss);
+            inv = r * (1.5 - 0.5 * ss * r * r);
+          }
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) uacc[e] += xe[e] * inv;
         }
       }
       if (PACK) {
@@ -151,37 +217,83 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
     for (int t = tid; t < 64 * D / 8; t += kThreads) *reinterpret_cast<Vec16*>(tail + (size_t)t * 8) = Vec16{{0u, 0u, 0u, 0u}};
   }
 
-  if (!want_mean) return;
+  if (!want_mean && !want_sics) return;
   // reduce over token slots: lanes with equal tid % TPT inside the wave ...
 #pragma unroll
   for (int off = TPT; off < 64; off <<= 1) {
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) acc[e] += __shfl_xor(acc[e], off);
+    for (int e = 0; e < EPV; ++e) {
+      acc[e] += __shfl_xor(acc[e], off);
+      if (want_sics) uacc[e] += __shfl_xor(uacc[e], off);
+    }
   }
   // ... then across the waves
   if (lane < TPT) {
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) red[wave][c0 + e] = acc[e];
+    for (int e = 0; e < EPV; ++e) {
+      red[wave][c0 + e] = acc[e];
+      if (want_sics) ured[wave][c0 + e] = uacc[e];
+    }
   }
   __syncthreads();
-  if (tid < D) {
+  if (tid < D && want_mean) {
     double s = 0.0;
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) s += red[w][tid];
     mean_out[((size_t)bh * g.nblk + j) * D + tid] = (float)(s / (double)box.n);
   }
+  if (want_sics) {
+    // |sum_i u_i|^2 over the D channels (threads tid < D), then / n^2
+    double u2 = 0.0;
+    if (tid < D) {
+      double u = 0.0;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) u += ured[w][tid];
+      u2 = u * u;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) u2 += __shfl_xor(u2, off);
+    __syncthreads();  // ured is reused below
+    if (lane == 0) ured[wave][0] = u2;
+    __syncthreads();
+    if (tid == 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) t += ured[w][0];
+      const double n = (double)box.n;
+      sics_out[(size_t)bh * g.nblk + j] = (float)(t / (n * n));
+    }
+  }
 }
 
-template <bool BF16, int D, bool PACK>
+template <bool BF16, int D, bool PACK, bool SICS = false>
 hipError_t launch_t(const Geom& g, const void* q, const void* k, const void* v, float* qm, float* km,
-                    void* qp, void* kp, void* vp, int roles, hipStream_t s) {
+                    void* qp, void* kp, void* vp, int roles, hipStream_t s, float* qs = nullptr,
+                    float* ks = nullptr) {
   dim3 grid(g.nblk, g.BH, roles);
-  summarize_kernel<BF16, D, PACK><<<grid, kThreads, 0, s>>>(
-      g, q, k, v, qm, km, (uint16_t*)qp, (uint16_t*)kp, (uint16_t*)vp);
+  summarize_kernel<BF16, D, PACK, SICS><<<grid, kThreads, 0, s>>>(
+      g, q, k, v, qm, km, (uint16_t*)qp, (uint16_t*)kp, (uint16_t*)vp, qs, ks);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_summarize_sics(const Geom& g, bool bf16, const void* q, const void* k, float* q_mean,
+                                 float* k_mean, float* q_sics, float* k_sics, hipStream_t s) {
+  if (g.BH == 0) return hipSuccess;
+  if (bf16) {
+    if (g.d == 128)
+      return launch_t<true, 128, false, true>(g, q, k, nullptr, q_mean, k_mean, nullptr, nullptr, nullptr, 2, s,
+                                              q_sics, k_sics);
+    return launch_t<true, 64, false, true>(g, q, k, nullptr, q_mean, k_mean, nullptr, nullptr, nullptr, 2, s,
+                                           q_sics, k_sics);
+  }
+  if (g.d == 128)
+    return launch_t<false, 128, false, true>(g, q, k, nullptr, q_mean, k_mean, nullptr, nullptr, nullptr, 2, s,
+                                             q_sics, k_sics);
+  return launch_t<false, 64, false, true>(g, q, k, nullptr, q_mean, k_mean, nullptr, nullptr, nullptr, 2, s,
+                                          q_sics, k_sics);
+}
 
 hipError_t launch_summarize(const Geom& g, bool bf16, const void* q, const void* k, const void* v,
                             float* q_mean, float* k_mean, void* qpack, void* kpack, void* vpack,

@@ -124,6 +124,12 @@ def test_compute_entry_points_reject_before_launch():
     with pytest.raises(spade.SpadeError) as e:
         spade.spade_summarize(p, 0, 0, 0, 0, stream=0)
     assert e.value.status == INVALID
+    with pytest.raises(spade.SpadeError) as e:
+        spade.spade_summarize_sics(p, 0, 0, 0, 0, 0, 0, stream=0)
+    assert e.value.status == INVALID
+    with pytest.raises(spade.SpadeError) as e:
+        spade.spade_summarize_sics(_prob(cfg, d=32), 1, 1, 1, 1, 0, 0, stream=0)
+    assert e.value.status == UNSUP
     b = spade.Budget("ratio", [0.25] * cfg.H)
     cap = spade.spade_max_nnz(p, b)
     with pytest.raises(spade.SpadeError) as e:
@@ -144,6 +150,7 @@ def test_empty_batch_is_a_noop():
     cfg = synth.get_config("small")
     p = _prob(cfg, B=0)
     spade.spade_summarize(p, 0, 0, 0, 0, stream=0)  # nothing to do, nothing launched
+    spade.spade_summarize_sics(p, 0, 0, 0, 0, 0, 0, stream=0)
     spade.spade_debug_scores(p, 0, 0, 0, stream=0)
 
 

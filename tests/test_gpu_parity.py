@@ -116,6 +116,75 @@ def test_summarize_matches_oracle(name):
         assert (np.abs(g - ref) <= ulp).all(), np.abs(g - ref).max()
 
 
+def oracle_sics(cfg, x):
+    g = geom(cfg)
+    out = np.empty((cfg.B, cfg.H, g.nblk))
+    for h in range(cfg.H):
+        out[:, h:h + 1] = oracle.sics(to_f64(cfg, x[:, h:h + 1]), g)
+    return out
+
+
+def assert_sics_close(got, ref, name):
+    """The GPU takes the online form |sum u|^2 / n^2 in fp64, the oracle the
+    pairwise sum: both round once to fp32, so they agree to an ulp of the
+    result (plus the fp64 cancellation of nearly balanced blocks)."""
+    g = got.cpu().numpy().astype(np.float64)
+    tol = np.abs(ref) * 2.0 ** -22 + 1e-12
+    bad = np.abs(g - ref) > tol
+    assert not bad.any(), f"{name}: {bad.sum()} blocks, max err {np.abs(g - ref).max()}"
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_summarize_sics_matches_oracle(name):
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    qd, kd = to_dev(cfg, x["q"]), to_dev(cfg, x["k"])
+    qm, km, qs, ks = spade.summarize_sics(qd, kd, grid, block)
+    qm0, km0 = spade.summarize(qd, kd, grid, block)
+    # the means are those of the plain summarize, bit for bit
+    assert torch.equal(qm, qm0) and torch.equal(km, km0)
+    assert_sics_close(qs, oracle_sics(cfg, x["q"]), name + " q")
+    assert_sics_close(ks, oracle_sics(cfg, x["k"]), name + " k")
+    assert (qs >= 0).all() and (qs <= 1 + 1e-6).all()
+
+
+def test_sics_closed_forms_on_device():
+    """Constructed fp32 tokens: a block of one repeated vector gives 1, a
+    block of opposite pairs gives 0, one live token among zeros gives 1/n^2,
+    orthogonal one-hot tokens give 1/n (exact in fp64, exact in fp32)."""
+    T, Hh, W, bt, bh, bw, d = 1, 1, 16, 1, 1, 4, 64
+    p_grid, p_block = (T, Hh, W), (bt, bh, bw)
+    x = np.zeros((1, 1, W, d), dtype=np.float32)
+    v = np.linspace(-1.0, 2.0, d).astype(np.float32)
+    x[0, 0, 0:4] = v                                   # block 0: same vector
+    x[0, 0, 4:8] = np.stack([v, -v, 2 * v, -v])        # block 1: cancels
+    x[0, 0, 9] = v                                     # block 2: one live token
+    x[0, 0, 12:16] = np.eye(d, dtype=np.float32)[:4] * 3.0  # block 3: orthogonal
+    xd = torch.from_numpy(x).cuda()
+    qm, km, qs, ks = spade.summarize_sics(xd, xd, p_grid, p_block)
+    got = qs.cpu().numpy()[0, 0]
+    np.testing.assert_allclose(got, [1.0, 0.0, 1.0 / 16, 0.25], rtol=2e-7, atol=1e-12)
+    assert torch.equal(qs, ks)
+
+
+def test_sics_outputs_are_optional():
+    cfg = synth.get_config("ragged_small")
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    qd, kd = to_dev(cfg, x["q"]), to_dev(cfg, x["k"])
+    p = spade.problem_for(qd, grid, block)
+    nblk = spade.spade_num_blocks(p)
+    qm = torch.empty(cfg.B, cfg.H, nblk, cfg.d, device="cuda")
+    km = torch.empty_like(qm)
+    ks = torch.full((cfg.B, cfg.H, nblk), -7.0, device="cuda")
+    spade.spade_summarize_sics(p, qd, kd, qm, km, None, ks)
+    torch.cuda.synchronize()
+    assert_sics_close(ks, oracle_sics(cfg, x["k"]), "k only")
+    qm0, km0 = spade.summarize(qd, kd, grid, block)
+    assert torch.equal(qm, qm0) and torch.equal(km, km0)
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_scores_and_selection_match_oracle(name):
     cfg = synth.get_config(name)
@@ -325,3 +394,16 @@ def test_full_size_selection_and_sampled_rows(name, ratio):
         worst = max(worst, np.abs(got - ref).max())
     print(f"[full] {cfg.name}: sampled rows {rows} max-abs {worst:.3e}", flush=True)
     assert worst <= BF16_TOL
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["mid", "ragged"])
+def test_full_size_sics_every_block(name):
+    cfg = synth.get_config(name)
+    print(f"[full sics] {cfg.name}", flush=True)
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    qm, km, qs, ks = spade.summarize_sics(to_dev(cfg, x["q"]), to_dev(cfg, x["k"]), grid, block)
+    assert_sics_close(qs, oracle_sics(cfg, x["q"]), name + " q")
+    assert_sics_close(ks, oracle_sics(cfg, x["k"]), name + " k")
+
