@@ -7,5 +7,5 @@ from .spade_oracle import *  # noqa: F401,F403
 from .spade_oracle import (  # noqa: F401
     Geometry, Selection, block_extents, block_tokens, token_block_ids, summarize, sics,
     default_scale, estimate, keep_count, select, attention, attention_block_row,
-    attention_full, dense_attention, spade_attn, MODE_COUNT, MODE_RATIO, MODE_MASS,
+    attention_full, dense_attention, spade_attn, MODE_COUNT, MODE_RATIO, MODE_MASS, SUMMARIZERS,
 )

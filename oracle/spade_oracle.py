@@ -21,7 +21,8 @@ pages are silent (each also listed in the design notes):
   block along an axis that the block size does not divide is partial; block
   j = (it*nH + ih)*nW + iw; Q and KV use the same tiling;
 * the Summarizer is the mean over the block's real tokens, computed exactly
-  and stored as fp32 (the summary tensor's storage type);
+  and stored as fp32 (the summary tensor's storage type); the max and min
+  Summarizers take the channel-wise extreme over the same tokens;
 * the intra-block estimate (SICS) of a block is the mean cosine similarity
   over all ordered pairs of its real tokens, diagonal included (zero tokens:
   cosine 0), so it lies in [0, 1];
@@ -115,20 +116,35 @@ def token_block_ids(g: Geometry) -> np.ndarray:
 # Summarizer (vDiT-SSR, Summarizer & Estimator Expressions): block mean
 # ---------------------------------------------------------------------------
 
-def summarize(x: np.ndarray, g: Geometry, store_f32: bool = True) -> np.ndarray:
-    """Block means of x [B, H, N, d] -> [B, H, nblk, d].
+SUMMARIZERS = ("mean", "max", "min")
 
-    The sum over the block's real tokens is taken in fp64 and divided once by
-    the token count; with store_f32 the mean is rounded to fp32 (returned as
-    fp64 holding fp32 values).
+
+def summarize(x: np.ndarray, g: Geometry, store_f32: bool = True, op: str = "mean") -> np.ndarray:
+    """Block summaries of x [B, H, N, d] -> [B, H, nblk, d].
+
+    The Summarizer reduces each block over its real tokens, channel by channel
+    (technical summary, "Methodology 1. vDiT-SSR", Summarizer & Estimator
+    Expressions: max, min or mean).  Mean: the sum is taken in fp64 and
+    divided once by the token count.  Max / min: the largest / smallest value
+    of each channel.  With store_f32 the summary is rounded to fp32 (returned
+    as fp64 holding fp32 values); max and min of bf16 or fp32 inputs are
+    exact.
     """
     x = np.asarray(x, dtype=np.float64)
     B, H, N, d = x.shape
     assert N == g.N
+    if op not in SUMMARIZERS:
+        raise ValueError(op)
     toks = block_tokens(g)
     out = np.empty((B, H, len(toks), d), dtype=np.float64)
     for j, tk in enumerate(toks):
-        out[:, :, j, :] = x[:, :, tk, :].sum(axis=2) / float(len(tk))
+        xb = x[:, :, tk, :]
+        if op == "mean":
+            out[:, :, j, :] = xb.sum(axis=2) / float(len(tk))
+        elif op == "max":
+            out[:, :, j, :] = xb.max(axis=2)
+        else:
+            out[:, :, j, :] = xb.min(axis=2)
     if store_f32:
         out = out.astype(np.float32).astype(np.float64)
     return out
@@ -345,12 +361,12 @@ def dense_attention(q, k, v, scale: float) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def spade_attn(q, k, v, g: Geometry, mode: str, per_head: Sequence[float],
-               scale: Optional[float] = None):
+               scale: Optional[float] = None, summarizer: str = "mean"):
     """Summaries -> scores -> selection -> attention.  Returns (O, Selection, S)."""
     d = q.shape[-1]
     scale = default_scale(d) if scale is None else float(scale)
-    qm = summarize(q, g)
-    km = summarize(k, g)
+    qm = summarize(q, g, op=summarizer)
+    km = summarize(k, g, op=summarizer)
     S = estimate(qm, km, scale)
     sel = select(S, mode, per_head)
     O = attention_full(q, k, v, g, sel.row_ptr, sel.col_idx, scale)

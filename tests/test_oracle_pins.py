@@ -427,6 +427,59 @@ def test_single_block_is_dense_within_that_block():
 
 
 # ---------------------------------------------------------------------------
+# max / min summarizers
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_p64", "mid_shape", "ragged_small"])
+def test_max_min_summary_closed_form_on_monotone_field(name):
+    """x[n, c] = a_c t + b_c h + e_c w + f_c is monotone along each axis, so its
+    block maximum sits at the corner that maximises each term (t1-1 where a_c > 0,
+    t0 where a_c < 0, ...) and the minimum at the opposite corner."""
+    cfg = synth.get_config(name)
+    g = Geometry(cfg.T, cfg.Hh, cfg.W, cfg.bt, cfg.bh, cfg.bw)
+    d = 8
+    rng = np.random.default_rng(1)
+    coef = rng.integers(-3, 4, size=(4, d)).astype(np.float64)
+    n = np.arange(g.N)
+    t, h, w = n // (g.Hh * g.W), (n // g.W) % g.Hh, n % g.W
+    x = (t[:, None] * coef[0] + h[:, None] * coef[1] + w[:, None] * coef[2] + coef[3])[None, None]
+    mx = oracle.summarize(x, g, store_f32=False, op="max")[0, 0]
+    mn = oracle.summarize(x, g, store_f32=False, op="min")[0, 0]
+    for j, (t0, t1, h0, h1, w0, w1) in enumerate(oracle.block_extents(g)):
+        lo = np.array([t0, h0, w0], dtype=np.float64)
+        hi = np.array([t1 - 1, h1 - 1, w1 - 1], dtype=np.float64)
+        a = coef[:3]
+        want_max = np.where(a > 0, hi[:, None], lo[:, None]) * a
+        want_min = np.where(a > 0, lo[:, None], hi[:, None]) * a
+        np.testing.assert_array_equal(mx[j], want_max.sum(0) + coef[3])
+        np.testing.assert_array_equal(mn[j], want_min.sum(0) + coef[3])
+
+
+def test_max_min_mean_order_and_duality():
+    cfg, g, x = _inputs("ragged_small")
+    q = x["q"]
+    mx = oracle.summarize(q, g, op="max")
+    mn = oracle.summarize(q, g, op="min")
+    me = oracle.summarize(q, g, store_f32=False)
+    assert (mn <= me + 1e-12).all() and (me <= mx + 1e-12).all()
+    np.testing.assert_array_equal(oracle.summarize(-q, g, op="min"), -mx)
+    # a single-token block: all three summarizers return that token
+    g1 = Geometry(2, 2, 2, 1, 1, 1)
+    y = np.random.default_rng(2).standard_normal((1, 1, 8, 4)).astype(np.float32).astype(np.float64)
+    for op in oracle.SUMMARIZERS:
+        np.testing.assert_array_equal(oracle.summarize(y, g1, op=op), y)
+
+
+def test_max_min_are_exact_block_extremes_by_bruteforce():
+    cfg, g, x = _inputs("tiny")
+    for op, fn in (("max", max), ("min", min)):
+        got = oracle.summarize(x["k"], g, op=op)
+        for j, tk in enumerate(oracle.block_tokens(g)):
+            for c in range(cfg.d):
+                assert got[0, 1, j, c] == fn(float(x["k"][0, 1, n, c]) for n in tk)
+
+
+# ---------------------------------------------------------------------------
 # intra-block estimate (SICS: Sum of Intra-block Cosine Similarities)
 # ---------------------------------------------------------------------------
 
@@ -575,4 +628,19 @@ def test_planted_sics_dot_products_instead_of_cosines_is_caught():
         return np.array([(y[0, 0, tk] @ y[0, 0, tk].T).sum() / len(tk) ** 2 for tk in toks])
 
     assert np.abs(bad(3.0 * q) - bad(q)).max() > 1e-3
+
+
+def test_planted_max_over_padded_box_is_caught():
+    """Taking the maximum over the full (bt, bh, bw) box instead of the block's
+    real tokens reads tokens of the next block on partial edges; the closed
+    form of the monotone field catches it."""
+    g = Geometry(3, 5, 4, 2, 2, 3)
+    n = np.arange(g.N)
+    t, h, w = n // (g.Hh * g.W), (n // g.W) % g.Hh, n % g.W
+    x = (t + 2.0 * h + 3.0 * w)[None, None, :, None]
+    good = oracle.summarize(x, g, store_f32=False, op="max")[0, 0, :, 0]
+    bad = []
+    for (t0, t1, h0, h1, w0, w1) in oracle.block_extents(g):
+        bad.append((t0 + g.bt - 1) + 2.0 * (h0 + g.bh - 1) + 3.0 * (w0 + g.bw - 1))
+    assert (np.array(bad) != good).any()
 
