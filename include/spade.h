@@ -65,15 +65,26 @@ typedef enum spade_keep_mode {
                            mass over all nblk blocks reaches tau_h, tau_h in (0, 1] */
 } spade_keep_mode;
 
+/* Summarizer of a block ("Methodology 1. vDiT-SSR", Summarizer & Estimator
+ * Expressions: the Summarizer reduces Q/K blocks, e.g. via max/min/mean). */
+typedef enum spade_summarizer {
+  SPADE_SUM_MEAN = 0, /* mean over the block's real tokens (exact sum, one division) */
+  SPADE_SUM_MAX = 1,  /* channel-wise maximum over the block's real tokens */
+  SPADE_SUM_MIN = 2   /* channel-wise minimum over the block's real tokens */
+} spade_summarizer;
+
 /* Shape of one attention layer.
  * Supported: d in {64, 128}; B*H >= 0; 1 <= nblk <= 4096; N == T*Hh*W;
- * bt*bh*bw <= 1024; B*H*nblk < 2^31 rows.  scale == 0 selects 1/sqrt(d). */
+ * bt*bh*bw <= 1024; B*H*nblk < 2^31 rows.  scale == 0 selects 1/sqrt(d).
+ * summarizer picks the block summary that every entry point computes and the
+ * Estimator uses (an unknown value is SPADE_ERR_INVALID_ARG). */
 typedef struct spade_problem {
   int32_t B, H, N, d;
   int32_t T, Hh, W;
   int32_t bt, bh, bw;
   int32_t dtype; /* spade_dtype */
   float scale;
+  int32_t summarizer; /* spade_summarizer; 0 (mean) for the default path */
 } spade_problem;
 
 /* Per-head keep budget: per_head is a HOST array of H values interpreted by

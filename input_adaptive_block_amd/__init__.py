@@ -10,7 +10,8 @@ from __future__ import annotations
 from typing import Optional, Sequence, Tuple
 
 from ._lib import (  # noqa: F401
-    EXPORTED, LIB_PATH, MODES, Budget, Problem, SpadeError, SPADE_BF16, SPADE_F32,
+    EXPORTED, LIB_PATH, MODES, SUMMARIZERS, Budget, Problem, SpadeError, SPADE_BF16, SPADE_F32,
+    SPADE_SUM_MAX, SPADE_SUM_MEAN, SPADE_SUM_MIN,
     SPADE_KEEP_COUNT, SPADE_KEEP_MASS, SPADE_KEEP_RATIO, SPADE_OK, SPADE_ERR_CAPACITY,
     SPADE_ERR_DEVICE, SPADE_ERR_INVALID_ARG, SPADE_ERR_UNSUPPORTED, lib, spade_attn,
     spade_block_sparse_attn, spade_check, spade_debug_scores, spade_estimate_select,
@@ -33,8 +34,10 @@ def _torch():
     return torch
 
 
-def problem_for(q, grid: Sequence[int], block: Sequence[int], scale: Optional[float] = None) -> Problem:
-    """Problem of a [B, H, N, d] tensor on grid (T, Hh, W) with block (bt, bh, bw)."""
+def problem_for(q, grid: Sequence[int], block: Sequence[int], scale: Optional[float] = None,
+                summarizer: str = "mean") -> Problem:
+    """Problem of a [B, H, N, d] tensor on grid (T, Hh, W) with block (bt, bh, bw);
+    summarizer is "mean", "max" or "min"."""
     torch = _torch()
     B, H, N, d = q.shape
     if q.dtype == torch.bfloat16:
@@ -45,7 +48,10 @@ def problem_for(q, grid: Sequence[int], block: Sequence[int], scale: Optional[fl
         raise SpadeError(SPADE_ERR_UNSUPPORTED, f"dtype {q.dtype}")
     T, Hh, W = grid
     bt, bh, bw = block
-    return Problem(B, H, N, d, T, Hh, W, bt, bh, bw, dt, 0.0 if scale is None else float(scale))
+    if summarizer not in SUMMARIZERS:
+        raise SpadeError(SPADE_ERR_INVALID_ARG, f"summarizer {summarizer!r}")
+    return Problem(B, H, N, d, T, Hh, W, bt, bh, bw, dt, 0.0 if scale is None else float(scale),
+                   SUMMARIZERS[summarizer])
 
 
 def _check_tensor(t, name, shape=None, dtype=None):
@@ -68,9 +74,9 @@ def alloc_workspace(problem: Problem, device=None):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def summarize(q, k, grid, block) -> Tuple["object", "object"]:
+def summarize(q, k, grid, block, summarizer: str = "mean") -> Tuple["object", "object"]:
     torch = _torch()
-    p = problem_for(q, grid, block)
+    p = problem_for(q, grid, block, summarizer=summarizer)
     nblk = spade_num_blocks(p)
     if nblk < 0:
         raise SpadeError(spade_check(p), "summarize")
@@ -82,11 +88,11 @@ def summarize(q, k, grid, block) -> Tuple["object", "object"]:
     return qm, km
 
 
-def summarize_sics(q, k, grid, block):
-    """Block means and the per-block intra-block cosine similarity (SICS, in
-    [0, 1]) of q and k: returns (q_mean, k_mean, q_sics, k_sics)."""
+def summarize_sics(q, k, grid, block, summarizer: str = "mean"):
+    """Block summaries and the per-block intra-block cosine similarity (SICS,
+    in [0, 1]) of q and k: returns (q_sum, k_sum, q_sics, k_sics)."""
     torch = _torch()
-    p = problem_for(q, grid, block)
+    p = problem_for(q, grid, block, summarizer=summarizer)
     nblk = spade_num_blocks(p)
     if nblk < 0:
         raise SpadeError(spade_check(p), "summarize_sics")
@@ -128,10 +134,11 @@ def block_sparse_attn(q, k, v, grid, block, row_ptr, col_idx, scale=None, worksp
     return o
 
 
-def attn(q, k, v, grid, block, mode, per_head: Sequence[float], scale=None, workspace=None):
+def attn(q, k, v, grid, block, mode, per_head: Sequence[float], scale=None, workspace=None,
+         summarizer: str = "mean"):
     """Whole path; returns (o, row_ptr, col_idx)."""
     torch = _torch()
-    p = problem_for(q, grid, block, scale)
+    p = problem_for(q, grid, block, scale, summarizer)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(t, name, q.shape, q.dtype)
     bud = Budget(mode, per_head)

@@ -30,6 +30,12 @@ SPADE_KEEP_MASS = 2
 
 MODES = {"count": SPADE_KEEP_COUNT, "ratio": SPADE_KEEP_RATIO, "mass": SPADE_KEEP_MASS}
 
+SPADE_SUM_MEAN = 0
+SPADE_SUM_MAX = 1
+SPADE_SUM_MIN = 2
+
+SUMMARIZERS = {"mean": SPADE_SUM_MEAN, "max": SPADE_SUM_MAX, "min": SPADE_SUM_MIN}
+
 
 class SpadeError(RuntimeError):
     def __init__(self, status: int, where: str = ""):
@@ -42,7 +48,7 @@ class _Problem(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
         ("T", ctypes.c_int32), ("Hh", ctypes.c_int32), ("W", ctypes.c_int32),
         ("bt", ctypes.c_int32), ("bh", ctypes.c_int32), ("bw", ctypes.c_int32),
-        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("summarizer", ctypes.c_int32),
     ]
 
 
@@ -64,10 +70,11 @@ class Problem:
     bw: int
     dtype: int = SPADE_BF16
     scale: float = 0.0
+    summarizer: int = SPADE_SUM_MEAN
 
     def c(self) -> _Problem:
         return _Problem(self.B, self.H, self.N, self.d, self.T, self.Hh, self.W,
-                        self.bt, self.bh, self.bw, self.dtype, self.scale)
+                        self.bt, self.bh, self.bw, self.dtype, self.scale, self.summarizer)
 
 
 class Budget:

@@ -19,6 +19,8 @@ spade_status make_geom(const spade_problem* p, Geom* g) {
   if (p->bt <= 0 || p->bh <= 0 || p->bw <= 0) return SPADE_ERR_INVALID_ARG;
   if (p->dtype != SPADE_BF16 && p->dtype != SPADE_F32) return SPADE_ERR_INVALID_ARG;
   if (!(p->scale >= 0.0f) || isinf(p->scale)) return SPADE_ERR_INVALID_ARG;  // NaN, <0, inf
+  if (p->summarizer != SPADE_SUM_MEAN && p->summarizer != SPADE_SUM_MAX && p->summarizer != SPADE_SUM_MIN)
+    return SPADE_ERR_INVALID_ARG;
   const long long N = (long long)p->T * p->Hh * p->W;
   if (N != (long long)p->N) return SPADE_ERR_INVALID_ARG;
   if (p->d != 64 && p->d != 128) return SPADE_ERR_UNSUPPORTED;
@@ -46,6 +48,7 @@ spade_status make_geom(const spade_problem* p, Geom* g) {
   g->BH = (int)BH;
   g->R = (int)R;
   g->bf16 = p->dtype == SPADE_BF16 ? 1 : 0;
+  g->op = p->summarizer;
   return SPADE_OK;
 }
 

@@ -23,6 +23,7 @@ struct Geom {
   int BH;     // B*H
   int R;      // B*H*nblk selection rows
   int bf16;   // 1: bf16 tensors (packed MFMA tiles), 0: fp32 debug path
+  int op;     // block summarizer: 0 mean, 1 max, 2 min
 };
 
 struct BlockBox {

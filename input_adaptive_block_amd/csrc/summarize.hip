@@ -70,6 +70,14 @@ __device__ inline double group_sum(double x) {
   return x;
 }
 
+// The Summarizer's reduction: sum (mean), maximum or minimum.
+__device__ inline double sum_op(int op, double a, double b) {
+  return op == 0 ? a + b : (op == 1 ? fmax(a, b) : fmin(a, b));
+}
+__device__ inline double sum_identity(int op) {
+  return op == 0 ? 0.0 : (op == 1 ? -__builtin_huge_val() : __builtin_huge_val());
+}
+
 __device__ inline float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ inline float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
@@ -111,11 +119,12 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
   __shared__ double ured[SICS ? kThreads / 64 : 1][SICS ? D : 1];
   __shared__ uint16_t vt[PACK ? 128 * VROW : 1];
 
+  const int op = g.op;  // the block summary: sum (mean), max or min over the real tokens
   double acc[EPV];
   double uacc[EPV];  // sum of the unit token vectors (SICS)
 #pragma unroll
   for (int e = 0; e < EPV; ++e) {
-    acc[e] = 0.0;
+    acc[e] = sum_identity(op);
     uacc[e] = 0.0;
   }
 
@@ -141,8 +150,10 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) xe[e] = (double)__uint_as_float(x.w[e]);
         }
+        if (l < box.n) {  // padded rows (zeros) take no part in a max or min
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[e] += xe[e];
+          for (int e = 0; e < EPV; ++e) acc[e] = sum_op(op, acc[e], xe[e]);
+        }
         if (want_sics) {
           // squared norm of the token over its TPT threads (consecutive lanes;
           // every thread of the group runs the same iterations)
@@ -223,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
   for (int off = TPT; off < 64; off <<= 1) {
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-      acc[e] += __shfl_xor(acc[e], off);
+      acc[e] = sum_op(op, acc[e], __shfl_xor(acc[e], off));
       if (want_sics) uacc[e] += __shfl_xor(uacc[e], off);
     }
   }
@@ -237,10 +248,10 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
   }
   __syncthreads();
   if (tid < D && want_mean) {
-    double s = 0.0;
+    double s = red[0][tid];
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) s += red[w][tid];
-    mean_out[((size_t)bh * g.nblk + j) * D + tid] = (float)(s / (double)box.n);
+    for (int w = 1; w < kThreads / 64; ++w) s = sum_op(op, s, red[w][tid]);
+    mean_out[((size_t)bh * g.nblk + j) * D + tid] = (float)(op == 0 ? s / (double)box.n : s);
   }
   if (want_sics) {
     // |sum_i u_i|^2 over the D channels (threads tid < D), then / n^2

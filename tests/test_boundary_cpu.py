@@ -111,6 +111,19 @@ def test_budget_rejections(mode, vals, status):
     assert spade.spade_check(p, b, -1) == status
 
 
+def test_summarizer_field_is_validated():
+    cfg = synth.get_config("mid")
+    for op in (spade.SPADE_SUM_MEAN, spade.SPADE_SUM_MAX, spade.SPADE_SUM_MIN):
+        assert spade.spade_check(_prob(cfg, summarizer=op), None, -1) == spade.SPADE_OK
+    for bad in (3, -1, 99):
+        p = _prob(cfg, summarizer=bad)
+        assert spade.spade_check(p, None, -1) == INVALID
+        assert spade.spade_num_blocks(p) == -1
+        with pytest.raises(spade.SpadeError) as e:
+            spade.spade_summarize(p, 1, 1, 1, 1, stream=0)  # rejected before any launch
+        assert e.value.status == INVALID
+
+
 def test_bad_mode_rejected():
     cfg = synth.get_config("mid")
     b = spade.Budget(9, [1.0] * cfg.H)

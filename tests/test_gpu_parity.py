@@ -116,6 +116,48 @@ def test_summarize_matches_oracle(name):
         assert (np.abs(g - ref) <= ulp).all(), np.abs(g - ref).max()
 
 
+def oracle_summaries(cfg, x, op):
+    g = geom(cfg)
+    out = np.empty((cfg.B, cfg.H, g.nblk, cfg.d))
+    for h in range(cfg.H):
+        out[:, h:h + 1] = oracle.summarize(to_f64(cfg, x[:, h:h + 1]), g, op=op)
+    return out
+
+
+@pytest.mark.parametrize("op", ["max", "min"])
+@pytest.mark.parametrize("name", SMALL)
+def test_max_min_summaries_are_exact(name, op):
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    qd, kd = to_dev(cfg, x["q"]), to_dev(cfg, x["k"])
+    qm, km = spade.summarize(qd, kd, grid, block, summarizer=op)
+    assert np.array_equal(qm.cpu().numpy().astype(np.float64), oracle_summaries(cfg, x["q"], op))
+    assert np.array_equal(km.cpu().numpy().astype(np.float64), oracle_summaries(cfg, x["k"], op))
+    # the SICS pass takes the same summarizer for its summary output
+    qm2, km2, qs, ks = spade.summarize_sics(qd, kd, grid, block, summarizer=op)
+    assert torch.equal(qm, qm2) and torch.equal(km, km2)
+
+
+@pytest.mark.parametrize("op", ["max", "min"])
+@pytest.mark.parametrize("name", ["mid_shape", "ragged_small", "tiny", "d64", "ragged_f32"])
+def test_whole_path_with_max_min_summarizer(name, op):
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    o, rp, ci = spade.attn(q, k, v, grid, block, cfg.mode, cfg.per_head_budget(), summarizer=op)
+    torch.cuda.synchronize()
+    rp, ci = csr_rows(rp, ci)
+    scale = oracle.default_scale(cfg.d)
+    S_ref = oracle.estimate(oracle_summaries(cfg, x["q"], op), oracle_summaries(cfg, x["k"], op), scale)
+    sel = oracle.select(S_ref, cfg.mode, cfg.per_head_budget())
+    compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), f"{name}/{op}")
+    ref = oracle.attention_full(*(to_f64(cfg, x[n]) for n in ("q", "k", "v")), geom(cfg), rp, ci, scale)
+    tol = BF16_TOL if cfg.dtype == "bf16" else F32_TOL
+    assert np.abs(dev_to_f64(o) - ref).max() <= tol
+
+
 def oracle_sics(cfg, x):
     g = geom(cfg)
     out = np.empty((cfg.B, cfg.H, g.nblk))
