@@ -31,6 +31,8 @@ pages are silent (each also listed in the design notes):
   budget keeps the first k (k = ceil(r*nK - 1e-6) clamped to [1, nK] for a
   ratio); a mass budget keeps the shortest prefix whose softmax(S) mass over
   all nK blocks reaches tau (at least one block);
+* an optional static window (radii in blocks along t, h, w) is united with
+  the blocks the budget keeps by score; with a window the budget may be 0;
 * attention is exact softmax attention of each query over all tokens of its
   kept KV blocks, renormalised over those keys only; every Q block is
   computed; output keeps the input raster layout.
@@ -204,19 +206,39 @@ def estimate(qm: np.ndarray, km: np.ndarray, scale: float) -> np.ndarray:
 # Index search: which KV blocks each Q block keeps
 # ---------------------------------------------------------------------------
 
-def keep_count(mode: str, value: float, nK: int) -> int:
-    """Blocks kept per row for a count or ratio budget."""
+def keep_count(mode: str, value: float, nK: int, allow_zero: bool = False) -> int:
+    """Blocks kept per row for a count or ratio budget.  With allow_zero (a
+    static window supplies the rest of the mask) a budget of 0 keeps no
+    block by score."""
+    lo = 0 if allow_zero else 1
     if mode == MODE_COUNT:
         k = int(value)
-        if k != value or k < 1 or k > nK:
-            raise ValueError("count budget must be an integer in [1, nK]")
+        if k != value or k < lo or k > nK:
+            raise ValueError(f"count budget must be an integer in [{lo}, nK]")
         return k
     if mode == MODE_RATIO:
         r = float(np.float32(value))
-        if not (0.0 < r <= 1.0):
+        if not ((0.0 < r or (allow_zero and r == 0.0)) and r <= 1.0):
             raise ValueError("ratio budget must be in (0, 1]")
-        return min(nK, max(1, math.ceil(r * nK - 1e-6)))
+        return min(nK, max(lo, math.ceil(r * nK - 1e-6)))
     raise ValueError(mode)
+
+
+def window_blocks(g: Geometry, i: int, radius: Sequence[int]) -> np.ndarray:
+    """Static window of Q block i: the KV blocks whose block coordinates differ
+    from i's by at most (rt, rh, rw) along (t, h, w), ascending ids
+    (technical summary, "Methodology 2. Scheme Generation", Policy Application:
+    the budget balances static windows and dynamic selection)."""
+    nT, nH, nW = g.counts
+    it, rem = divmod(i, nH * nW)
+    ih, iw = divmod(rem, nW)
+    rt, rh, rw = (int(r) for r in radius)
+    out = []
+    for jt in range(max(0, it - rt), min(nT, it + rt + 1)):
+        for jh in range(max(0, ih - rh), min(nH, ih + rh + 1)):
+            for jw in range(max(0, iw - rw), min(nW, iw + rw + 1)):
+                out.append((jt * nH + jh) * nW + jw)
+    return np.array(out, dtype=np.int64)
 
 
 @dataclass
@@ -231,8 +253,13 @@ class Selection:
         return self.col_idx[self.row_ptr[r]:self.row_ptr[r + 1]]
 
 
-def select(S: np.ndarray, mode: str, per_head: Sequence[float]) -> Selection:
-    """Select KV blocks per row of S [B, H, nQ, nK]; rows r = (b*H + h)*nQ + i."""
+def select(S: np.ndarray, mode: str, per_head: Sequence[float],
+           window: Optional[Sequence[int]] = None, g: Optional[Geometry] = None) -> Selection:
+    """Select KV blocks per row of S [B, H, nQ, nK]; rows r = (b*H + h)*nQ + i.
+
+    With a static window (radii (rt, rh, rw) in blocks; needs the geometry g)
+    the kept set of row i is the window of block i united with the blocks the
+    budget keeps by score; a budget of 0 then keeps the window alone."""
     B, H, nQ, nK = S.shape
     per_head = [float(np.float32(v)) for v in per_head]
     assert len(per_head) == H
@@ -244,14 +271,19 @@ def select(S: np.ndarray, mode: str, per_head: Sequence[float]) -> Selection:
     s_sorted = np.take_along_axis(S2, order, axis=1)
     counts = np.empty(R, dtype=np.int64)
     margins = np.empty(R, dtype=np.float64)
+    allow_zero = window is not None
     if mode in (MODE_COUNT, MODE_RATIO):
         for r in range(R):
-            k = keep_count(mode, per_head[head_of_row[r]], nK)
+            k = keep_count(mode, per_head[head_of_row[r]], nK, allow_zero)
             counts[r] = k
-            margins[r] = (s_sorted[r, k - 1] - s_sorted[r, k]) if k < nK else math.inf
+            margins[r] = (s_sorted[r, k - 1] - s_sorted[r, k]) if 0 < k < nK else math.inf
     elif mode == MODE_MASS:
         for r in range(R):
             tau = per_head[head_of_row[r]]
+            if allow_zero and tau == 0.0:
+                counts[r] = 0
+                margins[r] = math.inf
+                continue
             if not (0.0 < tau <= 1.0):
                 raise ValueError("mass budget must be in (0, 1]")
             # softmax of the row over all nK blocks, taken in descending order
@@ -269,11 +301,15 @@ def select(S: np.ndarray, mode: str, per_head: Sequence[float]) -> Selection:
             margins[r] = m
     else:
         raise ValueError(mode)
+    rows = [np.sort(order[r, :counts[r]]) for r in range(R)]
+    if window is not None:
+        assert g is not None and g.nblk == nQ == nK
+        for r in range(R):
+            rows[r] = np.union1d(rows[r], window_blocks(g, r % nQ, window))
+        counts = np.array([len(x) for x in rows], dtype=np.int64)
     row_ptr = np.zeros(R + 1, dtype=np.int64)
     row_ptr[1:] = np.cumsum(counts)
-    col_idx = np.empty(int(row_ptr[-1]), dtype=np.int64)
-    for r in range(R):
-        col_idx[row_ptr[r]:row_ptr[r + 1]] = np.sort(order[r, :counts[r]])
+    col_idx = np.concatenate(rows).astype(np.int64) if R else np.empty(0, dtype=np.int64)
     return Selection(row_ptr, col_idx, counts, margins, order)
 
 
@@ -361,13 +397,14 @@ def dense_attention(q, k, v, scale: float) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def spade_attn(q, k, v, g: Geometry, mode: str, per_head: Sequence[float],
-               scale: Optional[float] = None, summarizer: str = "mean"):
+               scale: Optional[float] = None, summarizer: str = "mean",
+               window: Optional[Sequence[int]] = None):
     """Summaries -> scores -> selection -> attention.  Returns (O, Selection, S)."""
     d = q.shape[-1]
     scale = default_scale(d) if scale is None else float(scale)
     qm = summarize(q, g, op=summarizer)
     km = summarize(k, g, op=summarizer)
     S = estimate(qm, km, scale)
-    sel = select(S, mode, per_head)
+    sel = select(S, mode, per_head, window, g)
     O = attention_full(q, k, v, g, sel.row_ptr, sel.col_idx, scale)
     return O, sel, S

@@ -480,6 +480,63 @@ def test_max_min_are_exact_block_extremes_by_bruteforce():
 
 
 # ---------------------------------------------------------------------------
+# static window united with the dynamic selection
+# ---------------------------------------------------------------------------
+
+def _block_coords_from_extents(g):
+    """Block coordinates from the token extents of each block (t0 // bt, ...)."""
+    return np.array([(t0 // g.bt, h0 // g.bh, w0 // g.bw) for (t0, t1, h0, h1, w0, w1) in oracle.block_extents(g)])
+
+
+def _static_mask(g, radius):
+    c = _block_coords_from_extents(g)
+    d = np.abs(c[:, None, :] - c[None, :, :])
+    return (d <= np.array(radius)[None, None, :]).all(axis=-1)  # [nQ, nK]
+
+
+@pytest.mark.parametrize("radius", [(0, 0, 0), (1, 0, 2), (2, 3, 1)])
+@pytest.mark.parametrize("mode,zero", [("count", 0), ("ratio", 0.0), ("mass", 0.0)])
+def test_zero_budget_with_window_is_the_static_mask(radius, mode, zero):
+    cfg, g, x = _inputs("ragged_small")
+    S = np.random.default_rng(5).standard_normal((cfg.B, cfg.H, g.nblk, g.nblk))
+    sel = oracle.select(S, mode, [zero] * cfg.H, window=radius, g=g)
+    m = _static_mask(g, radius)
+    for r in range(len(sel.counts)):
+        assert sel.row(r).tolist() == np.nonzero(m[r % g.nblk])[0].tolist()
+
+
+@pytest.mark.parametrize("mode,budget", [("count", 3), ("ratio", 0.2), ("mass", 0.7)])
+def test_window_unites_with_the_dynamic_selection(mode, budget):
+    cfg, g, x = _inputs("ragged_small")
+    S = np.random.default_rng(6).standard_normal((cfg.B, cfg.H, g.nblk, g.nblk))
+    radius = (1, 1, 0)
+    dyn = oracle.select(S, mode, [budget] * cfg.H)
+    hyb = oracle.select(S, mode, [budget] * cfg.H, window=radius, g=g)
+    m = _static_mask(g, radius)
+    for r in range(len(dyn.counts)):
+        want = sorted(set(dyn.row(r).tolist()) | set(np.nonzero(m[r % g.nblk])[0].tolist()))
+        assert hyb.row(r).tolist() == want
+        assert r % g.nblk in hyb.row(r)  # radius >= 0 always keeps the diagonal block
+
+
+def test_window_over_the_whole_grid_is_dense_attention():
+    cfg, g, x = _inputs("tiny")
+    nT, nH, nW = g.counts
+    O, sel, S = oracle.spade_attn(x["q"], x["k"], x["v"], g, "count", [0] * cfg.H,
+                                  window=(nT, nH, nW))
+    assert (sel.counts == g.nblk).all()
+    np.testing.assert_allclose(O, _sdpa(x["q"], x["k"], x["v"], oracle.default_scale(cfg.d)), atol=1e-12)
+
+
+def test_window_grows_with_its_radius():
+    g = Geometry(6, 7, 9, 2, 2, 3)
+    for i in range(g.nblk):
+        small = set(oracle.window_blocks(g, i, (1, 0, 1)).tolist())
+        big = set(oracle.window_blocks(g, i, (1, 1, 1)).tolist())
+        assert small <= big and i in small
+
+
+# ---------------------------------------------------------------------------
 # intra-block estimate (SICS: Sum of Intra-block Cosine Similarities)
 # ---------------------------------------------------------------------------
 
@@ -643,4 +700,15 @@ def test_planted_max_over_padded_box_is_caught():
     for (t0, t1, h0, h1, w0, w1) in oracle.block_extents(g):
         bad.append((t0 + g.bt - 1) + 2.0 * (h0 + g.bh - 1) + 3.0 * (w0 + g.bw - 1))
     assert (np.array(bad) != good).any()
+
+
+def test_planted_window_in_token_units_is_caught():
+    """Measuring the window radius in tokens instead of blocks keeps a
+    different set as soon as a block is longer than one token."""
+    g = Geometry(4, 6, 8, 2, 3, 4)
+    good = _static_mask(g, (1, 1, 1))
+    ext = oracle.block_extents(g)
+    c = np.array([(t0, h0, w0) for (t0, t1, h0, h1, w0, w1) in ext])
+    bad = (np.abs(c[:, None, :] - c[None, :, :]) <= 1).all(axis=-1)
+    assert (bad != good).any()
 
