@@ -88,10 +88,21 @@ typedef struct spade_problem {
 } spade_problem;
 
 /* Per-head keep budget: per_head is a HOST array of H values interpreted by
- * mode.  The same budget applies to every batch entry. */
+ * mode.  The same budget applies to every batch entry.
+ *
+ * Static window ("Methodology 2. Scheme Generation", Policy Application: the
+ * budget balances static windows and dynamic selection).  With
+ * window_enable != 0, Q block i at block coordinates (it, ih, iw) also keeps
+ * every KV block j with |jt-it| <= window_t, |jh-ih| <= window_h and
+ * |jw-iw| <= window_w (radii in blocks, >= 0, clipped to the grid): the kept
+ * set is that window united with the blocks the budget keeps by score.  With
+ * a window the budget values may also be 0 (count 0, ratio 0, mass 0: the
+ * window alone).  A zero-initialised budget has no window. */
 typedef struct spade_budget {
   int32_t mode; /* spade_keep_mode */
   const float* per_head;
+  int32_t window_enable;
+  int32_t window_t, window_h, window_w;
 } spade_budget;
 
 /* ---- host-only helpers (no device access) ------------------------------ */
@@ -99,8 +110,10 @@ typedef struct spade_budget {
 /* nblk of the problem, or -1 if the shape is invalid. */
 int32_t spade_num_blocks(const spade_problem* p);
 
-/* Entries col_idx must hold: exact for COUNT/RATIO, the worst case R*nblk
- * for MASS.  -1 if the problem or budget is invalid. */
+/* Entries col_idx must hold: exact for COUNT/RATIO without a window; with
+ * a window sum over rows of min(nblk, k + window size of the row's block)
+ * (exact when no scored block falls inside the window); the worst case
+ * R*nblk for MASS.  -1 if the problem or budget is invalid. */
 int64_t spade_max_nnz(const spade_problem* p, const spade_budget* budget);
 
 /* Bytes of device workspace that every compute entry point of this problem

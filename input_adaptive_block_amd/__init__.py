@@ -106,9 +106,10 @@ def summarize_sics(q, k, grid, block, summarizer: str = "mean"):
     return qm, km, qs, ks
 
 
-def estimate_select(q_mean, k_mean, problem: Problem, mode, per_head: Sequence[float], workspace=None):
+def estimate_select(q_mean, k_mean, problem: Problem, mode, per_head: Sequence[float], workspace=None,
+                    window=None):
     torch = _torch()
-    bud = Budget(mode, per_head)
+    bud = Budget(mode, per_head, window)
     cap = spade_max_nnz(problem, bud)
     if cap < 0:
         raise SpadeError(spade_check(problem, bud), "estimate_select")
@@ -135,13 +136,14 @@ def block_sparse_attn(q, k, v, grid, block, row_ptr, col_idx, scale=None, worksp
 
 
 def attn(q, k, v, grid, block, mode, per_head: Sequence[float], scale=None, workspace=None,
-         summarizer: str = "mean"):
-    """Whole path; returns (o, row_ptr, col_idx)."""
+         summarizer: str = "mean", window=None):
+    """Whole path; returns (o, row_ptr, col_idx).  window: None or the static
+    window's radii (rt, rh, rw) in blocks, united with the scored blocks."""
     torch = _torch()
     p = problem_for(q, grid, block, scale, summarizer)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(t, name, q.shape, q.dtype)
-    bud = Budget(mode, per_head)
+    bud = Budget(mode, per_head, window)
     cap = spade_max_nnz(p, bud)
     if cap < 0:
         raise SpadeError(spade_check(p, bud), "attn")

@@ -53,7 +53,9 @@ class _Problem(ctypes.Structure):
 
 
 class _Budget(ctypes.Structure):
-    _fields_ = [("mode", ctypes.c_int32), ("per_head", ctypes.POINTER(ctypes.c_float))]
+    _fields_ = [("mode", ctypes.c_int32), ("per_head", ctypes.POINTER(ctypes.c_float)),
+                ("window_enable", ctypes.c_int32), ("window_t", ctypes.c_int32),
+                ("window_h", ctypes.c_int32), ("window_w", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -78,12 +80,16 @@ class Problem:
 
 
 class Budget:
-    """Per-head keep budget (host memory, kept alive with the object)."""
+    """Per-head keep budget (host memory, kept alive with the object); window is
+    None or the static window's radii (rt, rh, rw) in blocks."""
 
-    def __init__(self, mode, per_head: Sequence[float]):
+    def __init__(self, mode, per_head: Sequence[float], window: Optional[Sequence[int]] = None):
         self.mode = MODES[mode] if isinstance(mode, str) else int(mode)
         self.values = (ctypes.c_float * max(1, len(per_head)))(*[float(v) for v in per_head])
-        self._c = _Budget(self.mode, ctypes.cast(self.values, ctypes.POINTER(ctypes.c_float)))
+        self.window = None if window is None else tuple(int(r) for r in window)
+        wt, wh, ww = self.window if self.window is not None else (0, 0, 0)
+        self._c = _Budget(self.mode, ctypes.cast(self.values, ctypes.POINTER(ctypes.c_float)),
+                          1 if self.window is not None else 0, wt, wh, ww)
 
     def c(self) -> _Budget:
         return self._c

@@ -52,13 +52,27 @@ spade_status make_geom(const spade_problem* p, Geom* g) {
   return SPADE_OK;
 }
 
-// Blocks per row for COUNT / RATIO (host arithmetic in double).
-int keep_k(int mode, float v, int nblk) {
+// Blocks per row for COUNT / RATIO (host arithmetic in double); with a window
+// a budget of 0 keeps no block by score.
+int keep_k(int mode, float v, int nblk, bool window) {
   if (mode == SPADE_KEEP_COUNT) return (int)v;
   long long k = (long long)ceil((double)v * nblk - 1e-6);
-  if (k < 1) k = 1;
+  const long long lo = window ? 0 : 1;
+  if (k < lo) k = lo;
   if (k > nblk) k = nblk;
   return (int)k;
+}
+
+// Number of blocks in the static window of block i (clipped to the grid).
+long long window_size(const Geom& g, int i, int wt, int wh, int ww) {
+  const int it = i / (g.nH * g.nW), rem = i - it * g.nH * g.nW;
+  const int ih = rem / g.nW, iw = rem - ih * g.nW;
+  auto span = [](int c, int r, int n) -> long long {
+    const long long lo = c - (long long)r < 0 ? 0 : c - (long long)r;
+    const long long hi = c + (long long)r > n - 1 ? n - 1 : c + (long long)r;
+    return hi - lo + 1;
+  };
+  return span(it, wt, g.nT) * span(ih, wh, g.nH) * span(iw, ww, g.nW);
 }
 
 spade_status check_budget(const spade_budget* bgt, const Geom& g) {
@@ -66,12 +80,15 @@ spade_status check_budget(const spade_budget* bgt, const Geom& g) {
   if (bgt->mode != SPADE_KEEP_COUNT && bgt->mode != SPADE_KEEP_RATIO && bgt->mode != SPADE_KEEP_MASS)
     return SPADE_ERR_INVALID_ARG;
   if (g.H > 0 && bgt->per_head == nullptr) return SPADE_ERR_INVALID_ARG;
+  const bool win = bgt->window_enable != 0;
+  if (win && (bgt->window_t < 0 || bgt->window_h < 0 || bgt->window_w < 0)) return SPADE_ERR_INVALID_ARG;
+  const float lo = win ? 0.0f : 1.0f;
   for (int h = 0; h < g.H; ++h) {
     const float v = bgt->per_head[h];
     if (!(v == v) || isinf(v)) return SPADE_ERR_INVALID_ARG;
     if (bgt->mode == SPADE_KEEP_COUNT) {
-      if (v != floorf(v) || v < 1.0f || v > (float)g.nblk) return SPADE_ERR_INVALID_ARG;
-    } else if (!(v > 0.0f && v <= 1.0f)) {
+      if (v != floorf(v) || v < lo || v > (float)g.nblk) return SPADE_ERR_INVALID_ARG;
+    } else if (!((v > 0.0f || (win && v == 0.0f)) && v <= 1.0f)) {
       return SPADE_ERR_INVALID_ARG;
     }
   }
@@ -80,9 +97,20 @@ spade_status check_budget(const spade_budget* bgt, const Geom& g) {
 
 long long max_nnz(const Geom& g, const spade_budget* bgt) {
   if (bgt->mode == SPADE_KEEP_MASS) return (long long)g.R * g.nblk;
+  const bool win = bgt->window_enable != 0;
   long long per_batch = 0;
-  for (int h = 0; h < g.H; ++h) per_batch += keep_k(bgt->mode, bgt->per_head[h], g.nblk);
-  return per_batch * g.nblk * g.B;
+  for (int h = 0; h < g.H; ++h) {
+    const long long k = keep_k(bgt->mode, bgt->per_head[h], g.nblk, win);
+    if (!win) {
+      per_batch += k * g.nblk;
+      continue;
+    }
+    for (int i = 0; i < g.nblk; ++i) {
+      const long long u = k + window_size(g, i, bgt->window_t, bgt->window_h, bgt->window_w);
+      per_batch += u < g.nblk ? u : g.nblk;
+    }
+  }
+  return per_batch * g.B;
 }
 
 int num_cus() {
@@ -128,12 +156,17 @@ SelectArgs make_select_args(const spade_budget* bgt, const Geom& g) {
   SelectArgs a;
   memset(&a, 0, sizeof(a));
   a.mode = bgt->mode;
+  const bool win = bgt->window_enable != 0;
   for (int h = 0; h < g.H; ++h) {
     if (bgt->mode == SPADE_KEEP_MASS)
       a.tau[h] = (double)bgt->per_head[h];
     else
-      a.k[h] = keep_k(bgt->mode, bgt->per_head[h], g.nblk);
+      a.k[h] = keep_k(bgt->mode, bgt->per_head[h], g.nblk, win);
   }
+  a.window = win ? 1 : 0;
+  a.wt = bgt->window_t;
+  a.wh = bgt->window_h;
+  a.ww = bgt->window_w;
   return a;
 }
 

@@ -225,6 +225,22 @@ __global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __res
     }
   }
 
+  if (a.window) {
+    // static window of this row's Q block, united with the scored set
+    const int i = row % nK;
+    const int it = i / (g.nH * g.nW), rem = i - it * g.nH * g.nW;
+    const int ih = rem / g.nW, iw = rem - ih * g.nW;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = 64 * e + lane;
+      if (j < nK) {
+        const int jt = j / (g.nH * g.nW), jr = j - jt * g.nH * g.nW;
+        const int jh = jr / g.nW, jw = jr - jh * g.nW;
+        if (abs(jt - it) <= a.wt && abs(jh - ih) <= a.wh && abs(jw - iw) <= a.ww) kept[e] = true;
+      }
+    }
+  }
+
   int cnt = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {

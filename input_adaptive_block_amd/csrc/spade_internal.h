@@ -61,8 +61,10 @@ __host__ __device__ inline int block_token(const Geom& g, const BlockBox& b, int
 // Budget as passed to the selection kernel (by value).
 struct SelectArgs {
   int mode;              // spade_keep_mode
-  int k[kMaxHeads];      // COUNT / RATIO: blocks per row of head h
-  double tau[kMaxHeads]; // MASS: threshold of head h
+  int k[kMaxHeads];      // COUNT / RATIO: blocks per row of head h (0: none by score)
+  double tau[kMaxHeads]; // MASS: threshold of head h (0: none by score)
+  int window;            // 1: unite the static window below with the scored set
+  int wt, wh, ww;        // window radii in blocks along t, h, w
 };
 
 // Workspace carve-up (byte offsets, 256-aligned).

@@ -124,6 +124,24 @@ def test_summarizer_field_is_validated():
         assert e.value.status == INVALID
 
 
+def test_window_budget_validation_and_capacity():
+    cfg = synth.get_config("ragged_small")
+    p = _prob(cfg)
+    g = oracle.Geometry(cfg.T, cfg.Hh, cfg.W, cfg.bt, cfg.bh, cfg.bw)
+    # a budget of 0 needs a window; radii must be >= 0
+    assert spade.spade_check(p, spade.Budget("count", [0] * cfg.H), -1) == INVALID
+    assert spade.spade_check(p, spade.Budget("ratio", [0.0] * cfg.H), -1) == INVALID
+    assert spade.spade_check(p, spade.Budget("count", [0] * cfg.H, (1, 0, 1)), -1) == spade.SPADE_OK
+    assert spade.spade_check(p, spade.Budget("mass", [0.0] * cfg.H, (0, 0, 0)), -1) == spade.SPADE_OK
+    assert spade.spade_check(p, spade.Budget("count", [2] * cfg.H, (1, -1, 0)), -1) == INVALID
+    # capacity with a window: sum over rows of min(nK, k + |window|)
+    for radius, k in (((0, 0, 0), 0), ((1, 2, 1), 3), ((9, 9, 9), 5)):
+        b = spade.Budget("count", [k] * cfg.H, radius)
+        sizes = [len(oracle.window_blocks(g, i, radius)) for i in range(g.nblk)]
+        want = cfg.B * cfg.H * sum(min(g.nblk, k + n) for n in sizes)
+        assert spade.spade_max_nnz(p, b) == want
+
+
 def test_bad_mode_rejected():
     cfg = synth.get_config("mid")
     b = spade.Budget(9, [1.0] * cfg.H)

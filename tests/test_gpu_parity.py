@@ -158,6 +158,33 @@ def test_whole_path_with_max_min_summarizer(name, op):
     assert np.abs(dev_to_f64(o) - ref).max() <= tol
 
 
+@pytest.mark.parametrize("window,scale_budget", [((0, 0, 0), 0.0), ((1, 1, 2), 0.0), ((1, 0, 1), 1.0),
+                                                  ((2, 2, 2), 1.0)])
+@pytest.mark.parametrize("name", ["mid_shape", "ragged_small", "tiny", "d64"])
+def test_static_window_united_with_selection(name, window, scale_budget):
+    """Budget 0 gives the static window alone; otherwise the window is united
+    with the scored blocks.  Selection is checked row by row, attention on
+    every output element."""
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    budget = [b * scale_budget for b in cfg.per_head_budget()]
+    if cfg.mode == "count":
+        budget = [int(b) for b in budget]
+    grid, block = grid_block(cfg)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    o, rp, ci = spade.attn(q, k, v, grid, block, cfg.mode, budget, window=window)
+    torch.cuda.synchronize()
+    rp, ci = csr_rows(rp, ci)
+    g = geom(cfg)
+    scale = oracle.default_scale(cfg.d)
+    S_ref = oracle.estimate(oracle_means(cfg, x["q"]), oracle_means(cfg, x["k"]), scale)
+    sel = oracle.select(S_ref, cfg.mode, budget, window=window, g=g)
+    compare_selection(sel, rp, ci, S_ref, cfg.mode, budget, f"{name}/{window}")
+    ref = oracle.attention_full(*(to_f64(cfg, x[n]) for n in ("q", "k", "v")), g, rp, ci, scale)
+    tol = BF16_TOL if cfg.dtype == "bf16" else F32_TOL
+    assert np.abs(dev_to_f64(o) - ref).max() <= tol
+
+
 def oracle_sics(cfg, x):
     g = geom(cfg)
     out = np.empty((cfg.B, cfg.H, g.nblk))
