@@ -8,4 +8,5 @@ from .spade_oracle import (  # noqa: F401
     Geometry, Selection, block_extents, block_tokens, token_block_ids, summarize, sics,
     default_scale, estimate, keep_count, select, window_blocks, attention, attention_block_row,
     attention_full, dense_attention, spade_attn, MODE_COUNT, MODE_RATIO, MODE_MASS, SUMMARIZERS,
+    scheme_aggregate, choose_scheme, spade_attn_schemes,
 )

@@ -408,3 +408,61 @@ def spade_attn(q, k, v, g: Geometry, mode: str, per_head: Sequence[float],
     sel = select(S, mode, per_head, window, g)
     O = attention_full(q, k, v, g, sel.row_ptr, sel.col_idx, scale)
     return O, sel, S
+
+
+# ---------------------------------------------------------------------------
+# Scheme generation: blocking candidates, head-wise choice, head grouping
+# ---------------------------------------------------------------------------
+
+def scheme_aggregate(q: np.ndarray, k: np.ndarray, T: int, Hh: int, W: int,
+                     candidates: Sequence[Tuple[int, int, int]]) -> np.ndarray:
+    """Aggregate SICS of every blocking candidate for every (b, h) -> [C, B, H].
+
+    Technical summary, "Methodology 2. Scheme Generation", Aggregation
+    Evaluation: every blocking candidate (Methodology 1, Blocking Scheme
+    Candidates) is scored by its SICS.  Here a candidate's score for one head
+    is the token-weighted mean of its per-block normalised SICS over Q and K,
+        A_c = sum_j n_j (sics_q[j] + sics_k[j]) / (2 N),
+    taken in fp64 over the fp32-stored per-block values (the type of the
+    per-block output).  A_c lies in [0, 1]; 1 means every block of the
+    candidate holds tokens that all point the same way.
+    """
+    out = []
+    for (bt, bh, bw) in candidates:
+        g = Geometry(T, Hh, W, bt, bh, bw)
+        n = np.array([len(t) for t in block_tokens(g)], dtype=np.float64)
+        sq = sics(q, g, store_f32=True)
+        sk = sics(k, g, store_f32=True)
+        out.append(((sq + sk) * n).sum(axis=-1) / (2.0 * g.N))
+    return np.stack(out)
+
+
+def choose_scheme(agg: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Policy Application: each head takes the candidate with the highest
+    aggregate score (ties to the earlier candidate).  Returns the choice
+    [B, H] and its margin over the runner-up (inf with one candidate)."""
+    choice = np.argmax(agg, axis=0)
+    if agg.shape[0] == 1:
+        return choice, np.full(choice.shape, math.inf)
+    srt = np.sort(agg, axis=0)
+    return choice, srt[-1] - srt[-2]
+
+
+def spade_attn_schemes(q, k, v, T: int, Hh: int, W: int, candidates: Sequence[Tuple[int, int, int]],
+                       mode: str, per_head: Sequence[float], scale: Optional[float] = None,
+                       summarizer: str = "mean", window: Optional[Sequence[int]] = None):
+    """Head-wise schemes: choose a blocking per (b, h), then run the path of
+    each head with its own blocking ("Head Grouping": heads that share a
+    scheme run together; the grouping changes no value).  Returns
+    (O, choice [B, H], aggregates [C, B, H])."""
+    agg = scheme_aggregate(q, k, T, Hh, W, candidates)
+    choice, _ = choose_scheme(agg)
+    B, H = q.shape[:2]
+    O = np.zeros(q.shape, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = Geometry(T, Hh, W, *candidates[choice[b, h]])
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            O[sl], _, _ = spade_attn(q[sl], k[sl], v[sl], g, mode, [per_head[h]], scale, summarizer, window)
+    return O, choice, agg
+

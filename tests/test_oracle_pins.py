@@ -614,6 +614,79 @@ def test_sics_invariant_to_token_scaling_and_rotation():
 
 
 # ---------------------------------------------------------------------------
+# scheme generation: blocking candidates and head-wise choice
+# ---------------------------------------------------------------------------
+
+def test_temporally_constant_field_chooses_the_temporal_blocking():
+    """x[t, h, w] = f(h, w): a candidate whose blocks span time only has SICS
+    exactly 1; a spatial candidate mixes different columns (aggregate < 1)."""
+    T, Hh, W, d = 4, 4, 6, 8
+    rng = np.random.default_rng(11)
+    col = rng.standard_normal((Hh * W, d))
+    x = np.tile(col, (T, 1))[None, None]                     # raster (t, h, w)
+    cands = [(1, 2, 3), (4, 1, 1), (2, 2, 2)]
+    agg = oracle.scheme_aggregate(x, x, T, Hh, W, cands)
+    assert agg[1, 0, 0] == pytest.approx(1.0, abs=1e-7)
+    assert agg[0, 0, 0] < 0.9 and agg[2, 0, 0] < 0.9
+    choice, margin = oracle.choose_scheme(agg)
+    assert choice[0, 0] == 1 and margin[0, 0] > 0.1
+
+
+def test_frame_constant_field_chooses_the_spatial_blocking():
+    T, Hh, W, d = 6, 3, 4, 8
+    rng = np.random.default_rng(12)
+    frame = rng.standard_normal((T, d))
+    x = np.repeat(frame, Hh * W, axis=0)[None, None]         # same vector in every token of a frame
+    cands = [(2, 1, 1), (1, 3, 4), (3, 3, 2)]
+    agg = oracle.scheme_aggregate(x, x, T, Hh, W, cands)
+    assert agg[1, 0, 0] == pytest.approx(1.0, abs=1e-7)
+    choice, _ = oracle.choose_scheme(agg)
+    assert choice[0, 0] == 1
+
+
+def test_scheme_aggregate_equals_pairwise_bruteforce():
+    T, Hh, W, d = 3, 4, 5, 6
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((1, 1, T * Hh * W, d))
+    k = rng.standard_normal((1, 1, T * Hh * W, d))
+    cands = [(2, 2, 2), (3, 1, 5)]
+    agg = oracle.scheme_aggregate(q, k, T, Hh, W, cands)
+    for c, blk in enumerate(cands):
+        g = Geometry(T, Hh, W, *blk)
+        tot = 0.0
+        for tk in oracle.block_tokens(g):
+            sq = float(np.float32(_sics_pairs(q[0, 0, tk])))
+            sk = float(np.float32(_sics_pairs(k[0, 0, tk])))
+            tot += len(tk) * (sq + sk)
+        assert agg[c, 0, 0] == pytest.approx(tot / (2 * g.N), rel=1e-12)
+
+
+def test_single_and_duplicate_candidates():
+    cfg, g, x = _inputs("tiny")
+    blk = (cfg.bt, cfg.bh, cfg.bw)
+    O1, ch1, _ = oracle.spade_attn_schemes(x["q"], x["k"], x["v"], cfg.T, cfg.Hh, cfg.W, [blk], cfg.mode,
+                                           cfg.per_head_budget())
+    O0, _, _ = oracle.spade_attn(x["q"], x["k"], x["v"], g, cfg.mode, cfg.per_head_budget())
+    assert (ch1 == 0).all()
+    np.testing.assert_array_equal(O1, O0)
+    agg = oracle.scheme_aggregate(x["q"], x["k"], cfg.T, cfg.Hh, cfg.W, [blk, blk])
+    choice, margin = oracle.choose_scheme(agg)
+    assert (choice == 0).all() and (margin == 0).all()   # a tie goes to the earlier candidate
+
+
+def test_each_head_equals_its_single_scheme_run():
+    cfg, g, x = _inputs("ragged_small")
+    cands = [(cfg.bt, cfg.bh, cfg.bw), (1, 4, 4), (4, 2, 2)]
+    O, choice, agg = oracle.spade_attn_schemes(x["q"], x["k"], x["v"], cfg.T, cfg.Hh, cfg.W, cands,
+                                               cfg.mode, cfg.per_head_budget())
+    for c, blk in enumerate(cands):
+        gc = Geometry(cfg.T, cfg.Hh, cfg.W, *blk)
+        Oc, _, _ = oracle.spade_attn(x["q"], x["k"], x["v"], gc, cfg.mode, cfg.per_head_budget())
+        m = choice == c
+        np.testing.assert_array_equal(O[m], Oc[m])
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by one of the pins above
 # ---------------------------------------------------------------------------
 
