@@ -234,6 +234,15 @@ def main():
     qs = torch.empty(cfg.B, cfg.H, nblk, dtype=torch.float32, device=dev)
     ks = torch.empty_like(qs)
     sics_ms = timed(lambda: spade.spade_summarize_sics(p, q, k, qm, km, qs, ks, stream))
+    # scheme generation over three blocking candidates of the layer's block size
+    # (the layer's own block, a wider-in-space and a longer-in-time one)
+    cands = [(cfg.bt, cfg.bh, cfg.bw), (max(1, cfg.bt // 2), cfg.bh, min(cfg.W, 2 * cfg.bw)),
+             (min(cfg.T, 2 * cfg.bt), max(1, cfg.bh // 2), cfg.bw)]
+    sws_n = spade.spade_schemes_workspace_bytes(p, cands)
+    sws = torch.empty(sws_n, dtype=torch.uint8, device=dev)
+    sagg = torch.empty(len(cands), cfg.B * cfg.H, dtype=torch.float32, device=dev)
+    ssch = torch.empty(cfg.B * cfg.H, dtype=torch.int32, device=dev)
+    scheme_ms = timed(lambda: spade.spade_scheme_select(p, q, k, cands, sagg, ssch, sws, sws_n, stream))
     sel_ms = timed(lambda: spade.spade_estimate_select(p, qm, km, bud, rp2, ci2, cap, ws, ws.numel(), stream))
     bsa_ms = timed(lambda: spade.spade_block_sparse_attn(p, q, k, v, rp, ci, cap, o2, ws, ws.numel(), stream))
     summ_bytes = 2 * q.numel() * q.element_size() + 2 * qm.numel() * 4
@@ -269,6 +278,7 @@ def main():
             "summarize_GBps": summ_bytes / (summ_ms * 1e-3) / 1e9,
             "summarize_with_sics": sics_ms,
             "summarize_with_sics_GBps": (summ_bytes + 2 * qs.numel() * 4) / (sics_ms * 1e-3) / 1e9,
+            "scheme_select_3_candidates": scheme_ms,
             "estimate_select": sel_ms,
             "block_sparse_attn_call": bsa_ms,
             "attention_kernel": attn_avg,

@@ -179,6 +179,42 @@ spade_status spade_attn(const spade_problem* p, const void* q, const void* k, co
                         const spade_budget* budget, void* o, int32_t* row_ptr, int32_t* col_idx,
                         int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- head-wise schemes ("Methodology 2. Scheme Generation"; "Head Grouping")
+ *
+ * A blocking candidate is a 3D block shape (Blocking Scheme Candidates).  The
+ * problem's own bt/bh/bw are ignored by these calls; every candidate must make
+ * a valid problem (else its status is returned).  At most 16 candidates. */
+typedef struct spade_block_shape {
+  int32_t bt, bh, bw;
+} spade_block_shape;
+
+/* Device workspace bytes of spade_scheme_select (budget NULL) or of
+ * spade_attn_schemes (its budget); 0 if anything is invalid. */
+size_t spade_schemes_workspace_bytes(const spade_problem* p, const spade_block_shape* candidates,
+                                     int32_t num_candidates, const spade_budget* budget);
+
+/* Aggregation Evaluation + Policy Application: for every (b, h) and every
+ * candidate c, agg[c, b*H+h] = sum_j n_j (q_sics_j + k_sics_j) / (2 N), the
+ * token-weighted mean of the per-block SICS of Q and K under that blocking
+ * (each per-block SICS as spade_summarize_sics stores it, fp32; the sum in
+ * fp64; agg stored as fp32, may be NULL); scheme[b*H+h] = the candidate with
+ * the largest aggregate in fp64, ties to the lower index.  candidates: HOST
+ * array; agg: device fp32 [C, B*H]; scheme: device int32 [B*H]. */
+spade_status spade_scheme_select(const spade_problem* p, const void* q, const void* k,
+                                 const spade_block_shape* candidates, int32_t num_candidates, float* agg,
+                                 int32_t* scheme, void* workspace, size_t ws_bytes, void* stream);
+
+/* Head-wise schemes end to end: spade_scheme_select, then for each candidate
+ * one launch segment of the whole path (summarize, estimate/select, block-
+ * sparse attention) over the heads that chose it (Head Grouping), each with
+ * its own blocking; every output element is written by exactly one segment.
+ * budget as for spade_attn, valid for every candidate's block count.  The
+ * CSR of each segment stays in the workspace.  No host synchronisation. */
+spade_status spade_attn_schemes(const spade_problem* p, const void* q, const void* k, const void* v,
+                                const spade_block_shape* candidates, int32_t num_candidates,
+                                const spade_budget* budget, void* o, float* agg, int32_t* scheme,
+                                void* workspace, size_t ws_bytes, void* stream);
+
 /* Measurement hook for benchmarks: while both events (hipEvent_t) are
  * non-NULL, every later spade_block_sparse_attn / spade_attn call on this host
  * thread records `start` just before and `stop` just after its flash

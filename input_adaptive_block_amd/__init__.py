@@ -15,17 +15,18 @@ from ._lib import (  # noqa: F401
     SPADE_KEEP_COUNT, SPADE_KEEP_MASS, SPADE_KEEP_RATIO, SPADE_OK, SPADE_ERR_CAPACITY,
     SPADE_ERR_DEVICE, SPADE_ERR_INVALID_ARG, SPADE_ERR_UNSUPPORTED, lib, spade_attn,
     spade_block_sparse_attn, spade_check, spade_debug_scores, spade_estimate_select,
-    spade_max_nnz, spade_num_blocks, spade_profile_events, spade_summarize, spade_summarize_sics,
+    spade_attn_schemes, spade_max_nnz, spade_num_blocks, spade_profile_events, spade_scheme_select,
+    spade_schemes_workspace_bytes, spade_summarize, spade_summarize_sics,
     spade_workspace_bytes,
     status_string,
 )
 
 __all__ = [
     "Problem", "Budget", "SpadeError", "problem_for", "summarize", "summarize_sics", "estimate_select",
-    "block_sparse_attn", "attn", "debug_scores", "alloc_workspace",
+    "block_sparse_attn", "attn", "debug_scores", "alloc_workspace", "scheme_select", "attn_schemes",
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
     "spade_summarize", "spade_summarize_sics", "spade_estimate_select", "spade_block_sparse_attn", "spade_attn",
-    "spade_debug_scores",
+    "spade_debug_scores", "spade_schemes_workspace_bytes", "spade_scheme_select", "spade_attn_schemes",
 ]
 
 
@@ -163,3 +164,40 @@ def debug_scores(q_mean, k_mean, problem: Problem):
     S = torch.empty(problem.B, problem.H, nblk, nblk, dtype=torch.float64, device=q_mean.device)
     spade_debug_scores(problem, q_mean, k_mean, S)
     return S
+
+
+def scheme_select(q, k, grid, candidates, summarizer: str = "mean"):
+    """Aggregate SICS of every blocking candidate per (b, h) and the head-wise
+    choice: returns (agg [C, B, H] fp32, scheme [B, H] int32)."""
+    torch = _torch()
+    p = problem_for(q, grid, candidates[0], summarizer=summarizer)
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", q.shape, q.dtype)
+    n = spade_schemes_workspace_bytes(p, candidates)
+    if n == 0:
+        raise SpadeError(SPADE_ERR_INVALID_ARG, "scheme_select")
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    agg = torch.empty(len(candidates), p.B, p.H, dtype=torch.float32, device=q.device)
+    scheme = torch.empty(p.B, p.H, dtype=torch.int32, device=q.device)
+    spade_scheme_select(p, q, k, candidates, agg, scheme, ws, ws.numel())
+    return agg, scheme
+
+
+def attn_schemes(q, k, v, grid, candidates, mode, per_head: Sequence[float], scale=None,
+                 summarizer: str = "mean", window=None):
+    """Head-wise schemes end to end: returns (o, scheme [B, H], agg [C, B, H])."""
+    torch = _torch()
+    p = problem_for(q, grid, candidates[0], scale, summarizer)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name, q.shape, q.dtype)
+    bud = Budget(mode, per_head, window)
+    n = spade_schemes_workspace_bytes(p, candidates, bud)
+    if n == 0:
+        raise SpadeError(SPADE_ERR_INVALID_ARG, "attn_schemes")
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    agg = torch.empty(len(candidates), p.B, p.H, dtype=torch.float32, device=q.device)
+    scheme = torch.empty(p.B, p.H, dtype=torch.int32, device=q.device)
+    spade_attn_schemes(p, q, k, v, candidates, bud, o, agg, scheme, ws, ws.numel())
+    return o, scheme, agg
+

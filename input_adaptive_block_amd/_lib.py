@@ -79,6 +79,18 @@ class Problem:
                         self.bt, self.bh, self.bw, self.dtype, self.scale, self.summarizer)
 
 
+class _BlockShape(ctypes.Structure):
+    _fields_ = [("bt", ctypes.c_int32), ("bh", ctypes.c_int32), ("bw", ctypes.c_int32)]
+
+
+def block_shapes(candidates: Sequence[Sequence[int]]):
+    """Host array of block shapes (bt, bh, bw) for the scheme entry points."""
+    arr = (_BlockShape * max(1, len(candidates)))()
+    for i, (bt, bh, bw) in enumerate(candidates):
+        arr[i] = _BlockShape(int(bt), int(bh), int(bw))
+    return arr
+
+
 class Budget:
     """Per-head keep budget (host memory, kept alive with the object); window is
     None or the static window's radii (rt, rh, rw) in blocks."""
@@ -122,6 +134,9 @@ def _load() -> ctypes.CDLL:
         "spade_block_sparse_attn": (st, [P, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
         "spade_attn": (st, [P, vp, vp, vp, Bp, vp, vp, vp, i64, vp, sz, vp]),
         "spade_debug_scores": (st, [P, vp, vp, vp, vp]),
+        "spade_schemes_workspace_bytes": (sz, [P, vp, ctypes.c_int32, Bp]),
+        "spade_scheme_select": (st, [P, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]),
+        "spade_attn_schemes": (st, [P, vp, vp, vp, vp, ctypes.c_int32, Bp, vp, vp, vp, vp, sz, vp]),
         "spade_profile_events": (None, [vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -137,6 +152,7 @@ EXPORTED = (
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
     "spade_status_string", "spade_summarize", "spade_summarize_sics", "spade_estimate_select",
     "spade_block_sparse_attn", "spade_attn", "spade_debug_scores", "spade_profile_events",
+    "spade_schemes_workspace_bytes", "spade_scheme_select", "spade_attn_schemes",
 )
 
 
@@ -233,3 +249,26 @@ def spade_debug_scores(problem: Problem, q_mean, k_mean, scores, stream=None) ->
 def spade_profile_events(start, stop) -> None:
     """Record hipEvent handles around every later attention kernel (None, None: off)."""
     _LIB.spade_profile_events(start, stop)
+
+
+def spade_schemes_workspace_bytes(problem: Problem, candidates, budget: Optional[Budget] = None) -> int:
+    arr = block_shapes(candidates)
+    return int(_LIB.spade_schemes_workspace_bytes(ctypes.byref(problem.c()), ctypes.cast(arr, ctypes.c_void_p),
+                                                  len(candidates), ctypes.byref(budget.c()) if budget else None))
+
+
+def spade_scheme_select(problem: Problem, q, k, candidates, agg, scheme, workspace, ws_bytes, stream=None) -> None:
+    arr = block_shapes(candidates)
+    _check(_LIB.spade_scheme_select(ctypes.byref(problem.c()), _ptr(q), _ptr(k), ctypes.cast(arr, ctypes.c_void_p),
+                                    len(candidates), _ptr(agg), _ptr(scheme), _ptr(workspace), ws_bytes,
+                                    _stream(stream)), "spade_scheme_select")
+
+
+def spade_attn_schemes(problem: Problem, q, k, v, candidates, budget: Budget, o, agg, scheme, workspace, ws_bytes,
+                       stream=None) -> None:
+    arr = block_shapes(candidates)
+    _check(_LIB.spade_attn_schemes(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v),
+                                   ctypes.cast(arr, ctypes.c_void_p), len(candidates), ctypes.byref(budget.c()),
+                                   _ptr(o), _ptr(agg), _ptr(scheme), _ptr(workspace), ws_bytes, _stream(stream)),
+           "spade_attn_schemes")
+

@@ -49,6 +49,8 @@ spade_status make_geom(const spade_problem* p, Geom* g) {
   g->R = (int)R;
   g->bf16 = p->dtype == SPADE_BF16 ? 1 : 0;
   g->op = p->summarizer;
+  g->hsel = nullptr;
+  g->hval = 0;
   return SPADE_OK;
 }
 
@@ -372,6 +374,154 @@ spade_status spade_debug_scores(const spade_problem* p, const float* q_mean, con
   if (g.BH == 0) return SPADE_OK;
   if (!q_mean || !k_mean || !scores) return SPADE_ERR_INVALID_ARG;
   return dev(launch_scores(g, q_mean, k_mean, est_scale(p), scores, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// scheme generation and head-wise schemes
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kMaxCandidates = 16;
+
+struct SchemeLayout {
+  size_t agg64;    // double [C * BH]
+  size_t qsics;    // float [BH * max nblk]
+  size_t ksics;    // float [BH * max nblk]
+  size_t row_ptr;  // int32 [BH * max nblk + 1]      (head-wise attention only)
+  size_t col_idx;  // int32 [max over candidates of the CSR capacity]
+  size_t pipe;     // the single-scheme workspace of the largest candidate
+  size_t total_select;
+  size_t total_attn;
+  long long cap;   // col_idx entries
+};
+
+spade_status scheme_geoms(const spade_problem* p, const spade_block_shape* cand, int C, Geom* gs) {
+  if (p == nullptr || cand == nullptr || C < 1) return SPADE_ERR_INVALID_ARG;
+  if (C > kMaxCandidates) return SPADE_ERR_UNSUPPORTED;
+  for (int c = 0; c < C; ++c) {
+    spade_problem pc = *p;
+    pc.bt = cand[c].bt;
+    pc.bh = cand[c].bh;
+    pc.bw = cand[c].bw;
+    SPADE_TRY(make_geom(&pc, &gs[c]));
+  }
+  return SPADE_OK;
+}
+
+// budget may be null (scheme selection only)
+spade_status scheme_layout(const Geom* gs, int C, const spade_budget* budget, SchemeLayout* L) {
+  int max_nblk = 0;
+  size_t pipe = 0;
+  long long cap = 0;
+  for (int c = 0; c < C; ++c) {
+    max_nblk = gs[c].nblk > max_nblk ? gs[c].nblk : max_nblk;
+    const size_t w = workspace_layout(gs[c]).total;
+    pipe = w > pipe ? w : pipe;
+    if (budget) {
+      SPADE_TRY(check_budget(budget, gs[c]));
+      const long long n = max_nnz(gs[c], budget);
+      if (n >= (1LL << 31)) return SPADE_ERR_UNSUPPORTED;
+      cap = n > cap ? n : cap;
+    }
+  }
+  const Geom& g = gs[0];
+  size_t off = 0;
+  L->agg64 = off; off = align256(off + (size_t)C * g.BH * 8);
+  L->qsics = off; off = align256(off + (size_t)g.BH * max_nblk * 4);
+  L->ksics = off; off = align256(off + (size_t)g.BH * max_nblk * 4);
+  L->total_select = off;
+  L->row_ptr = off; off = align256(off + ((size_t)g.BH * max_nblk + 1) * 4);
+  L->col_idx = off; off = align256(off + (size_t)(cap > 0 ? cap : 1) * 4);
+  L->pipe = off; off = align256(off + pipe);
+  L->total_attn = off;
+  L->cap = cap;
+  return SPADE_OK;
+}
+
+spade_status run_scheme_select(const spade_problem* p, const Geom* gs, int C, const SchemeLayout& L,
+                               const void* q, const void* k, float* agg, int32_t* scheme, void* ws,
+                               hipStream_t s) {
+  double* agg64 = reinterpret_cast<double*>(ws_ptr(ws, L.agg64));
+  float* qs = reinterpret_cast<float*>(ws_ptr(ws, L.qsics));
+  float* ks = reinterpret_cast<float*>(ws_ptr(ws, L.ksics));
+  const bool bf16 = p->dtype == SPADE_BF16;
+  for (int c = 0; c < C; ++c) {
+    SPADE_TRY(dev(launch_summarize_sics(gs[c], bf16, q, k, nullptr, nullptr, qs, ks, s)));
+    SPADE_TRY(dev(launch_scheme_aggregate(gs[c], qs, ks, c, agg64, agg, s)));
+  }
+  return dev(launch_scheme_choose(gs[0].BH, C, agg64, scheme, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spade_schemes_workspace_bytes(const spade_problem* p, const spade_block_shape* candidates,
+                                     int32_t num_candidates, const spade_budget* budget) {
+  Geom gs[kMaxCandidates];
+  if (scheme_geoms(p, candidates, num_candidates, gs) != SPADE_OK) return 0;
+  SchemeLayout L;
+  if (scheme_layout(gs, num_candidates, budget, &L) != SPADE_OK) return 0;
+  return budget ? L.total_attn : L.total_select;
+}
+
+spade_status spade_scheme_select(const spade_problem* p, const void* q, const void* k,
+                                 const spade_block_shape* candidates, int32_t num_candidates, float* agg,
+                                 int32_t* scheme, void* workspace, size_t ws_bytes, void* stream) {
+  Geom gs[kMaxCandidates];
+  SPADE_TRY(scheme_geoms(p, candidates, num_candidates, gs));
+  SchemeLayout L;
+  SPADE_TRY(scheme_layout(gs, num_candidates, nullptr, &L));
+  if (ws_bytes < L.total_select) return SPADE_ERR_CAPACITY;
+  if (gs[0].BH == 0) return SPADE_OK;
+  if (!q || !k || !scheme || !workspace) return SPADE_ERR_INVALID_ARG;
+  return run_scheme_select(p, gs, num_candidates, L, q, k, agg, scheme, workspace, (hipStream_t)stream);
+}
+
+spade_status spade_attn_schemes(const spade_problem* p, const void* q, const void* k, const void* v,
+                                const spade_block_shape* candidates, int32_t num_candidates,
+                                const spade_budget* budget, void* o, float* agg, int32_t* scheme,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  Geom gs[kMaxCandidates];
+  SPADE_TRY(scheme_geoms(p, candidates, num_candidates, gs));
+  if (budget == nullptr) return SPADE_ERR_INVALID_ARG;
+  SchemeLayout L;
+  SPADE_TRY(scheme_layout(gs, num_candidates, budget, &L));
+  if (ws_bytes < L.total_attn) return SPADE_ERR_CAPACITY;
+  if (gs[0].BH == 0) return SPADE_OK;
+  if (!q || !k || !v || !o || !scheme || !workspace) return SPADE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  SPADE_TRY(run_scheme_select(p, gs, num_candidates, L, q, k, agg, scheme, workspace, s));
+  // one launch segment per candidate over the heads that chose it
+  int32_t* row_ptr = reinterpret_cast<int32_t*>(ws_ptr(workspace, L.row_ptr));
+  int32_t* col_idx = reinterpret_cast<int32_t*>(ws_ptr(workspace, L.col_idx));
+  void* pw = ws_ptr(workspace, L.pipe);
+  const float scale = attn_scale(p);
+  for (int c = 0; c < num_candidates; ++c) {
+    Geom g = gs[c];
+    g.hsel = scheme;
+    g.hval = c;
+    const Workspace W = workspace_layout(g);
+    float* qm = reinterpret_cast<float*>(ws_ptr(pw, W.qmean));
+    float* km = reinterpret_cast<float*>(ws_ptr(pw, W.kmean));
+    if (p->dtype == SPADE_BF16) {
+      void* qp = ws_ptr(pw, W.qpack);
+      void* kp = ws_ptr(pw, W.kpack);
+      void* vp = ws_ptr(pw, W.vpack);
+      SPADE_TRY(dev(launch_summarize(g, true, q, k, v, qm, km, qp, kp, vp, s)));
+      SPADE_TRY(run_select(p, g, W, qm, km, budget, row_ptr, col_idx, pw, s));
+      SPADE_TRY(dev(launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, L.cap, scale, o,
+                                       reinterpret_cast<int*>(ws_ptr(pw, W.queue)), num_cus(), s)));
+    } else {
+      SPADE_TRY(dev(launch_summarize(g, false, q, k, nullptr, qm, km, nullptr, nullptr, nullptr, s)));
+      SPADE_TRY(run_select(p, g, W, qm, km, budget, row_ptr, col_idx, pw, s));
+      SPADE_TRY(dev(launch_bsattn_f32(g, (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
+                                      L.cap, scale, (float*)o, s)));
+    }
+  }
+  return SPADE_OK;
 }
 
 }  // extern "C"

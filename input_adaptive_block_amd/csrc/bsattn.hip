@@ -240,6 +240,11 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     const int bh = unit / um.per_head;
     const int pi = unit - bh * um.per_head;
     const size_t head_off = (size_t)bh * g.nblk * (size_t)g.P * D;
+    if (!head_active(g, bh)) {
+      // another scheme's head: nothing to compute or write; s_unit is reused
+      __syncthreads();
+      continue;
+    }
 
     // ---- the unit's union list of kept blocks, with member masks ----
     for (int t = tid; t < g.nblk; t += kThreads) {
@@ -485,6 +490,7 @@ __global__ __launch_bounds__(kF32Threads) void bsattn_f32_kernel(
   const int row = blockIdx.x;
   const int bh = row / g.nblk;
   const int i = row - bh * g.nblk;
+  if (!head_active(g, bh)) return;  // another scheme's head (whole workgroup)
   const BlockBox qbox = block_box(g, i);
   const int qi = blockIdx.y * kF32Threads + threadIdx.x;
   const bool active = qi < qbox.n;

@@ -36,6 +36,7 @@ __global__ __launch_bounds__(256) void scores_kernel(Geom g, const float* __rest
   __shared__ float qs[kSRows * LD];
   __shared__ float ks[kSCols * LD];
   const int bh = blockIdx.z;
+  if (!head_active(g, bh)) return;  // another scheme's head (whole workgroup)
   const int row0 = blockIdx.x * kSRows, col0 = blockIdx.y * kSCols;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = g.nblk;
@@ -139,6 +140,13 @@ __global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __res
   if (row >= g.R) return;  // whole wave exits together
   const int nK = g.nblk;
   const int h = (row / nK) % g.H;
+  if (!head_active(g, row / nK)) {
+    // another scheme's head: an empty row (its scores were never computed)
+    uint32_t* mrow = mask + (size_t)row * mask_words;
+    for (int w = lane; w < mask_words; w += 64) mrow[w] = 0u;
+    if (lane == 0) counts[row] = 0;
+    return;
+  }
   const double* Sr = S + (size_t)row * nK;
 
   uint64_t key[E];
@@ -256,6 +264,54 @@ __global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __res
 }
 
 // ---------------------------------------------------------------------------
+// scheme generation: aggregate SICS per candidate and head, head-wise argmax
+// ---------------------------------------------------------------------------
+constexpr int kAggThreads = 256;
+
+// A_c[bh] = sum_j n_j (q_sics[bh][j] + k_sics[bh][j]) / (2 N), fp64
+__global__ __launch_bounds__(kAggThreads) void scheme_aggregate_kernel(Geom g, const float* __restrict__ qs,
+                                                                      const float* __restrict__ ks, int c,
+                                                                      double* __restrict__ agg64,
+                                                                      float* __restrict__ agg) {
+  __shared__ double part[kAggThreads / 64];
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  double s = 0.0;
+  for (int j = tid; j < g.nblk; j += kAggThreads) {
+    const size_t at = (size_t)bh * g.nblk + j;
+    s += (double)block_box(g, j).n * ((double)qs[at] + (double)ks[at]);
+  }
+  s = wave_sum(s);
+  if ((tid & 63) == 0) part[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kAggThreads / 64; ++w) t += part[w];
+    const double a = t / (2.0 * (double)g.N);
+    agg64[(size_t)c * g.BH + bh] = a;
+    if (agg) agg[(size_t)c * g.BH + bh] = (float)a;
+  }
+}
+
+// scheme[bh] = argmax_c A_c[bh], ties to the lower c
+__global__ __launch_bounds__(256) void scheme_choose_kernel(int BH, int C, const double* __restrict__ agg64,
+                                                            int* __restrict__ scheme) {
+  const int bh = blockIdx.x * 256 + threadIdx.x;
+  if (bh >= BH) return;
+  int best = 0;
+  double bv = agg64[bh];
+  for (int c = 1; c < C; ++c) {
+    const double v = agg64[(size_t)c * BH + bh];
+    if (v > bv) {
+      bv = v;
+      best = c;
+    }
+  }
+  scheme[bh] = best;
+}
+
+// ---------------------------------------------------------------------------
 // CSR
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 1024;
@@ -305,6 +361,19 @@ __global__ __launch_bounds__(256) void compact_kernel(Geom g, const int* __restr
 }
 
 }  // namespace
+
+hipError_t launch_scheme_aggregate(const Geom& g, const float* q_sics, const float* k_sics, int c,
+                                   double* agg64, float* agg, hipStream_t s) {
+  if (g.BH == 0) return hipSuccess;
+  scheme_aggregate_kernel<<<g.BH, kAggThreads, 0, s>>>(g, q_sics, k_sics, c, agg64, agg);
+  return hipGetLastError();
+}
+
+hipError_t launch_scheme_choose(int BH, int C, const double* agg64, int* scheme, hipStream_t s) {
+  if (BH == 0) return hipSuccess;
+  scheme_choose_kernel<<<(BH + 255) / 256, 256, 0, s>>>(BH, C, agg64, scheme);
+  return hipGetLastError();
+}
 
 hipError_t launch_scores(const Geom& g, const float* q_mean, const float* k_mean, double scale,
                          double* scores, hipStream_t s) {

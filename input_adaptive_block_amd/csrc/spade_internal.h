@@ -24,7 +24,15 @@ struct Geom {
   int R;      // B*H*nblk selection rows
   int bf16;   // 1: bf16 tensors (packed MFMA tiles), 0: fp32 debug path
   int op;     // block summarizer: 0 mean, 1 max, 2 min
+  // head filter of a scheme's launch segment: when hsel is set, only the
+  // (b, h) pairs with hsel[b*H + h] == hval are computed (device array)
+  const int* hsel;
+  int hval;
 };
+
+__host__ __device__ inline bool head_active(const Geom& g, int bh) {
+  return g.hsel == nullptr || g.hsel[bh] == g.hval;
+}
 
 struct BlockBox {
   int t0, h0, w0;  // origin
@@ -92,6 +100,11 @@ hipError_t launch_summarize(const Geom& g, bool bf16, const void* q, const void*
 // pointer may be null)
 hipError_t launch_summarize_sics(const Geom& g, bool bf16, const void* q, const void* k, float* q_mean,
                                  float* k_mean, float* q_sics, float* k_sics, hipStream_t s);
+// scheme generation: aggregate SICS of candidate c for every (b, h) from the
+// per-block SICS of Q and K, and the head-wise argmax over the candidates
+hipError_t launch_scheme_aggregate(const Geom& g, const float* q_sics, const float* k_sics, int c,
+                                   double* agg64, float* agg, hipStream_t s);
+hipError_t launch_scheme_choose(int BH, int C, const double* agg64, int* scheme, hipStream_t s);
 hipError_t launch_scores(const Geom& g, const float* q_mean, const float* k_mean, double scale,
                          double* scores, hipStream_t s);
 hipError_t launch_select(const Geom& g, const double* scores, const SelectArgs& a, int* counts,

@@ -97,6 +97,7 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
   const int j = blockIdx.x;
   const int bh = blockIdx.y;
   const int role = blockIdx.z;
+  if (!head_active(g, bh)) return;  // another scheme's head (whole workgroup)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;

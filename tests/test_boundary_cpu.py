@@ -142,6 +142,34 @@ def test_window_budget_validation_and_capacity():
         assert spade.spade_max_nnz(p, b) == want
 
 
+def test_scheme_entry_points_validate_before_launch():
+    cfg = synth.get_config("small")
+    p = _prob(cfg)
+    good = [(cfg.bt, cfg.bh, cfg.bw), (1, 6, 8)]
+    assert spade.spade_schemes_workspace_bytes(p, good) > 0
+    b = spade.Budget("ratio", [0.25] * cfg.H)
+    assert spade.spade_schemes_workspace_bytes(p, good, b) > spade.spade_schemes_workspace_bytes(p, good)
+    assert spade.spade_schemes_workspace_bytes(p, [(0, 1, 1)]) == 0           # invalid candidate
+    assert spade.spade_schemes_workspace_bytes(p, []) == 0                    # no candidate
+    assert spade.spade_schemes_workspace_bytes(p, [(1, 1, 1)] * 17) == 0      # too many
+    # a count larger than one candidate's block count is invalid for the whole call
+    coarse = (3, 30, 11)
+    nb = spade.spade_num_blocks(_prob(cfg, bt=3, bh=30, bw=11))
+    assert 0 < nb < 40
+    assert spade.spade_schemes_workspace_bytes(p, good, spade.Budget("count", [40] * cfg.H)) > 0
+    assert spade.spade_schemes_workspace_bytes(p, good + [coarse], spade.Budget("count", [40] * cfg.H)) == 0
+    with pytest.raises(spade.SpadeError) as e:
+        spade.spade_scheme_select(p, 0, 0, good, 0, 0, 0, 0, stream=0)
+    assert e.value.status == CAP
+    n = spade.spade_schemes_workspace_bytes(p, good)
+    with pytest.raises(spade.SpadeError) as e:
+        spade.spade_scheme_select(p, 0, 0, good, 0, 0, 0, n, stream=0)
+    assert e.value.status == INVALID
+    with pytest.raises(spade.SpadeError) as e:
+        spade.spade_attn_schemes(p, 0, 0, 0, good, b, 0, 0, 0, 0, 0, stream=0)
+    assert e.value.status == CAP
+
+
 def test_bad_mode_rejected():
     cfg = synth.get_config("mid")
     b = spade.Budget(9, [1.0] * cfg.H)

@@ -476,3 +476,83 @@ def test_full_size_sics_every_block(name):
     assert_sics_close(qs, oracle_sics(cfg, x["q"]), name + " q")
     assert_sics_close(ks, oracle_sics(cfg, x["k"]), name + " k")
 
+
+# ---------------------------------------------------------------------------
+# head-wise schemes: blocking candidates, scheme choice, head grouping
+# ---------------------------------------------------------------------------
+
+def candidates_for(cfg):
+    c0 = (cfg.bt, cfg.bh, cfg.bw)
+    c1 = (max(1, cfg.bt // 2), cfg.bh, min(cfg.W, 2 * cfg.bw))
+    c2 = (min(cfg.T, 2 * cfg.bt), max(1, cfg.bh // 2), cfg.bw)
+    return [c0, c1, c2]
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_shape", "ragged_small", "d64", "ragged_f32"])
+def test_scheme_select_matches_oracle(name):
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    cands = candidates_for(cfg)
+    qd, kd = to_dev(cfg, x["q"]), to_dev(cfg, x["k"])
+    agg, scheme = spade.scheme_select(qd, kd, (cfg.T, cfg.Hh, cfg.W), cands)
+    ref = oracle.scheme_aggregate(to_f64(cfg, x["q"]), to_f64(cfg, x["k"]), cfg.T, cfg.Hh, cfg.W, cands)
+    np.testing.assert_allclose(agg.cpu().numpy().astype(np.float64), ref, rtol=1e-6, atol=1e-9)
+    choice, margin = oracle.choose_scheme(ref)
+    got = scheme.cpu().numpy()
+    # both sides decide in fp64 over the same fp32 per-block values
+    assert ((got == choice) | (margin <= 1e-9)).all()
+
+
+def test_scheme_choice_follows_constructed_fields():
+    """Tokens constant along time pick the temporal blocking; tokens constant
+    within each frame pick the spatial one (aggregate 1 exactly)."""
+    T, Hh, W, d = 4, 8, 8, 64
+    rng = np.random.default_rng(21)
+    col = rng.standard_normal((Hh * W, d)).astype(np.float32)
+    frame = rng.standard_normal((T, d)).astype(np.float32)
+    x = np.stack([np.tile(col, (T, 1)), np.repeat(frame, Hh * W, axis=0)])[None]  # [1, 2, N, d]
+    xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    cands = [(4, 1, 1), (1, 2, 2), (2, 1, 2)]
+    agg, scheme = spade.scheme_select(xd, xd, (T, Hh, W), cands)
+    a = agg.cpu().numpy()
+    assert scheme.cpu().tolist() == [[0, 1]]
+    assert abs(a[0, 0, 0] - 1.0) < 1e-6 and abs(a[1, 0, 1] - 1.0) < 1e-6
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_shape", "ragged_small", "ragged_f32"])
+def test_attn_schemes_matches_oracle_and_single_scheme_runs(name):
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    cands = candidates_for(cfg)
+    grid = (cfg.T, cfg.Hh, cfg.W)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    o, scheme, agg = spade.attn_schemes(q, k, v, grid, cands, cfg.mode, cfg.per_head_budget())
+    torch.cuda.synchronize()
+    sch = scheme.cpu().numpy()
+    # per head: bit for bit the single-scheme run with that head's blocking
+    for c, blk in enumerate(cands):
+        oc, _, _ = spade.attn(q, k, v, grid, blk, cfg.mode, cfg.per_head_budget())
+        m = torch.from_numpy(sch == c).cuda()
+        assert torch.equal(o[m], oc[m]), f"{name}: heads of candidate {c}"
+    # and against the oracle's head-wise path (its own scheme choice)
+    ref, choice, _ = oracle.spade_attn_schemes(*(to_f64(cfg, x[n]) for n in ("q", "k", "v")), cfg.T, cfg.Hh,
+                                               cfg.W, cands, cfg.mode, cfg.per_head_budget())
+    _, margin = oracle.choose_scheme(oracle.scheme_aggregate(to_f64(cfg, x["q"]), to_f64(cfg, x["k"]),
+                                                             cfg.T, cfg.Hh, cfg.W, cands))
+    same = (sch == choice)
+    assert (same | (margin <= 1e-9)).all()
+    tol = BF16_TOL if cfg.dtype == "bf16" else F32_TOL
+    of = dev_to_f64(o)
+    assert np.abs(of[same] - ref[same]).max() <= tol
+
+
+def test_single_candidate_equals_the_plain_path():
+    cfg = synth.get_config("mid_shape")
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    o1, scheme, agg = spade.attn_schemes(q, k, v, grid, [block], cfg.mode, cfg.per_head_budget())
+    o0, _, _ = spade.attn(q, k, v, grid, block, cfg.mode, cfg.per_head_budget())
+    assert (scheme == 0).all()
+    assert torch.equal(o1, o0)
+
