@@ -7,16 +7,19 @@
 // launch to raise occupancy ("Head Grouping").  The pages' kernel targets
 // Hopper (TMA, warp-group MMA); this one is written for CDNA4:
 //
-// * Work unit = two consecutive (row, 128-query tile) items of one head --
+// * Work unit = three consecutive (row, 128-query tile) items of one head --
 //   neighbouring Q blocks, whose kept KV sets overlap heavily.  The unit
 //   streams the UNION of their kept blocks once (ascending block id); each
-//   half of the workgroup (4 wavefronts x 32 queries) computes only on the
-//   blocks its own row keeps.  Every K/V byte fetched serves both tiles where
-//   they agree, which halves the L2 / Infinity-Cache traffic on video layers.
-// * One persistent workgroup of 8 wavefronts per CU pulls units from eight
-//   contiguous queues (one per XCD, equal shares of kept blocks); a workgroup
-//   starts on queue blockIdx % 8 and steals from the next queues when its own
-//   is empty, so neighbouring Q blocks of a head share one XCD's L2.
+//   third of the workgroup (4 wavefronts x 32 queries) computes only on the
+//   blocks its own row keeps.  A K/V byte fetched once serves every tile of
+//   the unit that keeps its block, which cuts L2 / Infinity-Cache traffic on
+//   video layers, where neighbouring rows keep mostly the same blocks.
+// * One persistent workgroup of 12 wavefronts per CU (three per SIMD) pulls
+//   units from eight contiguous queues (one per XCD, equal shares of kept
+//   blocks); a workgroup starts on queue blockIdx % 8 and steals from the next
+//   queues when its own is empty, so neighbouring Q blocks of a head share one
+//   XCD's L2.  With three wavefronts per SIMD, one wave's softmax runs beside
+//   the others' MFMAs.
 // * Scores are computed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_bf16: each lane owns one query and 16 keys, so the row
 //   max and row sum are in-lane plus one permlane32 swap, and the S^T
@@ -24,15 +27,26 @@
 //   O^T += V^T P^T.  Q operands stay in registers for the unit.
 // * K and V come pre-packed (by the summarize kernel) in MFMA operand order:
 //   a stage (two 32-key subtiles of K and of V, 32 KB at d = 128) is a
-//   contiguous HBM -> LDS copy issued with global_load_lds_dwordx4, and every
-//   LDS operand read is a contiguous 1 KB ds_read_b128 per wavefront (no bank
-//   conflicts).  Four stage buffers form a ring: three stages are in flight
-//   while one is computed.
+//   contiguous HBM -> LDS copy issued with global_load_lds_dwordx4 by eight
+//   of the wavefronts, and every LDS operand read is a contiguous 1 KB
+//   ds_read_b128 per wavefront (no bank conflicts).  Four stage slots form a
+//   ring with one barrier per stage: stage s is computed while stages s+1 to
+//   s+3 are in flight.  Each copying wave issues stage s+3 into the slot of
+//   stage s-1 right after its own steps of stage s (every wave left that
+//   slot before the barrier of stage s), so the copies are issued while the
+//   other waves still compute.  Operands are read just ahead of their MFMAs
+//   into small register rings, which keeps a wavefront within the 168
+//   registers that three wavefronts per SIMD allow.
+// * A wavefront raises its issue priority for its runs of MFMAs, so a wave
+//   that reaches its MFMAs keeps the matrix pipe while the others run their
+//   softmax arithmetic beside it.
 // * fp32 online softmax in the exp2 domain with log2(e) folded into the scale;
 //   the running max only moves when a score exceeds it by more than 2^8, which
 //   bounds every p by 256 (exact in value, fewer rescales of the 64-register O
 //   accumulator).  p is rounded to bf16 once and the row sum adds exactly the
-//   rounded values, so normalisation matches the weights PV used.
+//   rounded values, so normalisation matches the weights PV used.  The PV
+//   MFMAs of the first 16 keys of a lane run while the exp of its second 16
+//   is computed.
 #include "spade_internal.h"
 
 namespace spade {
@@ -43,7 +57,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kMembers = 2;                       // query tiles per work unit
+constexpr int kMembers = 3;                       // query tiles per work unit
+constexpr int kCopyWaves = 8;                     // waves that issue the stage copies
 constexpr int kWavesPerMember = 4;                // 4 x 32 queries = one 128-query tile
 constexpr int kWaves = kMembers * kWavesPerMember;
 constexpr int kThreads = 64 * kWaves;
@@ -51,11 +66,11 @@ constexpr int kQTile = 32 * kWavesPerMember;
 constexpr float kLazy = 8.0f;                     // log2 headroom before a rescale
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-// Work units: the (row, q-tile) items of one head in order, two at a time.
+// Work units: the (row, q-tile) items of one head in order, kMembers at a time.
 struct UnitMap {
   int nqt;         // q-tiles per row
   int items;       // items per head = nblk * nqt
-  int per_head;    // units per head = ceil(items / 2)
+  int per_head;    // units per head = ceil(items / kMembers)
 };
 
 __host__ __device__ inline UnitMap unit_map(const Geom& g) {
@@ -167,20 +182,10 @@ __device__ inline Stage next_stage(const Geom& g, const uint16_t* ul, const uint
   return st;
 }
 
-// Wait until at most `stages` stages of this wave's copies (PER instructions
-// each) are still in flight.  s_waitcnt immediate on gfx9: vmcnt in bits 3:0
+// s_waitcnt immediate on gfx9: vmcnt in bits 3:0
 // and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima (no wait).
 constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-template <int PER>
-__device__ inline void wait_copies(int stages) {
-  if (stages >= 2)
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * PER));
-  else if (stages == 1)
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(PER));
-  else
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-}
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
@@ -189,17 +194,14 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     long long cap, float scale_log2, uint16_t* __restrict__ out, int* __restrict__ queue, int U) {
   constexpr int SUB = 32 * D;                  // bf16 elements of one 32-key subtile
   constexpr int STAGE_KB = 2 * SUB * 2 / 1024;  // 1 KB copies per tensor per stage (2 subtiles)
-  constexpr int CPW = STAGE_KB / kWaves;       // copies per wave per tensor
+  constexpr int CPW = STAGE_KB / kCopyWaves;   // copies per copying wave per tensor
   constexpr int PER = 2 * CPW;                 // copy instructions per wave per stage
   constexpr int NC = D / 16;                   // K-chunks of S^T
   constexpr int NM = D / 32;                   // channel tiles of O^T
-  static_assert(STAGE_KB % kWaves == 0, "stage copies split evenly over the waves");
-  // four stage buffers as distinct objects, so the compiler can tell the
-  // in-flight copies into three of them from the operand reads of the fourth
-  __shared__ __attribute__((aligned(1024))) uint16_t kv0[2][2 * SUB];  // [K,V][2 subtiles]
-  __shared__ __attribute__((aligned(1024))) uint16_t kv1[2][2 * SUB];
-  __shared__ __attribute__((aligned(1024))) uint16_t kv2[2][2 * SUB];
-  __shared__ __attribute__((aligned(1024))) uint16_t kv3[2][2 * SUB];
+  static_assert(STAGE_KB % kCopyWaves == 0, "stage copies split evenly over the copying waves");
+  // four stage slots; the copies into them are issued from inline asm, so the
+  // compiler does not order the slot being read behind the copies in flight
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[4 * 2 * 2 * SUB];  // [slot][K,V][2 subtiles]
   __shared__ uint8_t flags[kMembers][kMaxBlocks];
   __shared__ uint16_t ulist[kMaxBlocks];
   __shared__ uint16_t ublkn[kMaxBlocks];  // tokens of each union entry's block
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: member tests stay scalar
   const int half = lane >> 5;
   const int member = wave / kWavesPerMember;
   const int lw = wave - member * kWavesPerMember;
@@ -248,8 +250,8 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
 
     // ---- the unit's union list of kept blocks, with member masks ----
     for (int t = tid; t < g.nblk; t += kThreads) {
-      flags[0][t] = 0;
-      flags[1][t] = 0;
+#pragma unroll
+      for (int m = 0; m < kMembers; ++m) flags[m][t] = 0;
     }
     __syncthreads();
 #pragma unroll
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     const int per = (g.nblk + kThreads - 1) / kThreads;
     const int jb = min(g.nblk, tid * per), je = min(g.nblk, jb + per);
     int cnt = 0;
-    for (int j = jb; j < je; ++j) cnt += (flags[0][j] | flags[1][j]) != 0;
+    for (int j = jb; j < je; ++j) cnt += (flags[0][j] | flags[1][j] | flags[2][j]) != 0;
     scanbuf[tid] = cnt;
     __syncthreads();
     for (int off = 1; off < kThreads; off <<= 1) {
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     {
       int w = scanbuf[tid] - cnt;
       for (int j = jb; j < je; ++j) {
-        const int msk = flags[0][j] | (flags[1][j] << 1);
+        const int msk = flags[0][j] | (flags[1][j] << 1) | (flags[2][j] << 2);
         if (msk) {
           ublkn[w] = (uint16_t)block_box(g, j).n;
           ulist[w++] = (uint16_t)(j | (msk << 12));
@@ -305,146 +307,185 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
 #pragma unroll
       for (int c = 0; c < NC; ++c) qop[c] = *reinterpret_cast<const bf16x8*>(qp + ((size_t)c * 64 + lane) * 8);
     }
+    // the Q loads are the only loads the compiler tracks; retire them here so
+    // that no wait inside the pipeline (which would also drain the stage
+    // copies in flight) is needed for them
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     f32x16 acc[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
-    float mref = -__builtin_huge_valf();
+    // running max (exp2 domain); finite so that the first rescale factor is 0
+    float mref = -1e30f;
     float lsum = 0.f;
-
-    // asynchronous HBM -> LDS copy of a stage: always two subtiles (the pack
-    // buffers carry one spare subtile at their end), wave w copies KB
-    // w*CPW .. w*CPW+CPW-1 of K and of V; lane L's 16 bytes land at 16 L
-    auto issue = [&](const Stage& st, uint16_t (&buf)[2][2 * SUB]) {
+    // asynchronous HBM -> LDS copy of a stage into ring slot `slot`: always
+    // two subtiles (the pack buffers carry one spare subtile at their end);
+    // wave w copies KB w*CPW .. w*CPW+CPW-1 of K and of V, lane L's 16 bytes
+    // land at 16 L.  M0 holds the wave's LDS destination.
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)ring;
+    auto issue = [&](const Stage& st, int slot) __attribute__((always_inline)) {
       const size_t src = head_off + (size_t)st.j * g.P * D + (size_t)st.s0 * SUB;
       const char* ks = reinterpret_cast<const char*>(kpack + src) + lane * 16;
       const char* vs = reinterpret_cast<const char*>(vpack + src) + lane * 16;
+      if (wave >= kCopyWaves) return;
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
         const int t = wave * CPW + c;
-        __builtin_amdgcn_global_load_lds(ks + t * 1024, (lds_void*)(&buf[0][t * 512]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vs + t * 1024, (lds_void*)(&buf[1][t * 512]), 16, 0, 0);
+        const uint32_t kd = __builtin_amdgcn_readfirstlane(ring_lds + (uint32_t)(slot * 4 * SUB + t * 512) * 2u);
+        const uint32_t vd = kd + 2 * SUB * 2;
+        const char* kg = ks + t * 1024;
+        const char* vg = vs + t * 1024;
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(kg), "s"(kd) : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vg), "s"(vd) : "memory", "m0");
       }
     };
-
-    // one stage: S^T, online softmax and O^T update for each of its subtiles
-    // pieces of one subtile: operand reads + S^T, masked row max with the rare
-    // rescale, and exp + PV
-    auto qk = [&](const uint16_t* kb, const uint16_t* vb, f32x16& sc, bf16x8 (&vop)[2 * NM]) {
-      const bf16x8* kl = reinterpret_cast<const bf16x8*>(kb);
-      const bf16x8* vl = reinterpret_cast<const bf16x8*>(vb);
-      bf16x8 kop[NC];
+    // One subtile of 32 keys at element offsets kx (K) / vx (V) of the ring:
+    // S^T = K Q^T (8 MFMAs; each K operand read two MFMAs ahead into a ring of
+    // three), the key mask of a partial subtile, the row max with the rare
+    // lazy rescale, p = exp2(S scale - m) rounded to bf16 and its row sum,
+    // then O^T += V^T P^T (8 MFMAs; V operands read two MFMAs ahead).  Three
+    // wavefronts per SIMD overlap one wave's softmax with the others' MFMAs.
+    auto step = [&](int kvalid, int kx, int vx) __attribute__((always_inline)) {
+      const bf16x8* kl = reinterpret_cast<const bf16x8*>(ring + kx);
+      const bf16x8* vl = reinterpret_cast<const bf16x8*>(ring + vx);
+      bf16x8 kr[3];
+      kr[0] = kl[lane];
+      kr[1] = kl[64 + lane];
+      f32x16 sx;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kop[c] = kl[c * 64 + lane];
+      for (int v = 0; v < 16; ++v) sx[v] = 0.f;
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int c = 0; c < 2 * NM; ++c) vop[c] = vl[c * 64 + lane];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sc[v] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qop[c], sc, 0, 0, 0);
-    };
-    auto max_rescale = [&](f32x16& sc, int kvalid) {
+      for (int c = 0; c < NC; ++c) {
+        if (c + 2 < NC) kr[(c + 2) % 3] = kl[(c + 2) * 64 + lane];
+        sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[c % 3], qop[c], sx, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      // V operand order of the PV MFMAs: i -> (channel tile i % NM, key chunk i / NM)
+      bf16x8 vr[3];
+      vr[0] = vl[(2 * (0 % NM) + 0 / NM) * 64 + lane];
+      vr[1] = vl[(2 * (1 % NM) + 1 / NM) * 64 + lane];
       if (kvalid < 32) {
         const int kk = kvalid - 4 * half;  // key of element v: 8 (v/4) + 4 half + v%4
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (8 * (v >> 2) + (v & 3) >= kk) sc[v] = -__builtin_huge_valf();
+          if (8 * (v >> 2) + (v & 3) >= kk) sx[v] = -__builtin_huge_valf();
       }
-      float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
-#pragma unroll
-      for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, sc[v]), sc[v + 1]);
-      mx = fmaxf(mx, sc[15]);
+      // row max as a tree of depth three (the scores are finite or -inf)
+      auto max3 = [](float a, float b, float c) __attribute__((always_inline)) {
+        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+      };
+      const float m0 = max3(sx[0], sx[1], sx[2]), m1 = max3(sx[3], sx[4], sx[5]);
+      const float m2 = max3(sx[6], sx[7], sx[8]), m3 = max3(sx[9], sx[10], sx[11]);
+      const float m4 = max3(sx[12], sx[13], sx[14]);
+      float mx = __builtin_elementwise_maximum(max3(m0, m1, m2), max3(m3, m4, sx[15]));
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       const float mnew = mx * scale_log2;
-      if (mnew > mref + kLazy) {
-        const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+      const bool need = mnew > mref + kLazy;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
         lsum *= alpha;
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[m][v] *= alpha;
-        mref = mnew;
+        mref = need ? mnew : mref;
       }
-    };
-    auto expp = [&](const f32x16& sc, bf16x8& pk0, bf16x8& pk1) {
+      // first half of the weights (keys of the first 16-key chunk), then the
+      // PV MFMAs of that chunk with the second half's exp beside them, then
+      // those of the second chunk with the row sum beside them
       bf16x2 pr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * e], scale_log2, -mref));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * e + 1], scale_log2, -mref));
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[2 * e], scale_log2, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[2 * e + 1], scale_log2, -mref));
         pr[e][0] = (__bf16)p0;
         pr[e][1] = (__bf16)p1;
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
       }
-      pk0 = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
-                                    __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-      pk1 = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
-                                    __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    auto pv = [&](const bf16x8 (&vop)[2 * NM], const bf16x8& pk0, const bf16x8& pk1) {
+      const bf16x8 pk0 = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                                 __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4,
+                                                 5, 6, 7);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m * 2 + 0], pk0, acc[m], 0, 0, 0);
+      for (int i = 0; i < NM; ++i) {
+        if (i + 2 < 2 * NM) vr[(i + 2) % 3] = vl[(2 * ((i + 2) % NM) + (i + 2) / NM) * 64 + lane];
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % 3], pk0, acc[i], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m * 2 + 1], pk1, acc[m], 0, 0, 0);
+        for (int e = 4 + i * 4 / NM; e < 4 + (i + 1) * 4 / NM; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[2 * e], scale_log2, -mref));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[2 * e + 1], scale_log2, -mref));
+          pr[e][0] = (__bf16)p0;
+          pr[e][1] = (__bf16)p1;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bf16x8 pk1 = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
+                                                 __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3), 0, 1, 2, 3, 4,
+                                                 5, 6, 7);
+#pragma unroll
+      for (int i = NM; i < 2 * NM; ++i) {
+        const int m = i - NM;
+        if (i + 2 < 2 * NM) vr[(i + 2) % 3] = vl[(2 * ((i + 2) % NM) + (i + 2) / NM) * 64 + lane];
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % 3], pk1, acc[m], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = (i - NM) * 8 / NM; e < (i - NM + 1) * 8 / NM; ++e)
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
     };
 
-    // one stage of this wave's row.  With two subtiles, the second S^T is
-    // issued in the same basic block as the first exp (independent work the
-    // scheduler can interleave) and the first PV.
-    auto compute = [&](const Stage& sg, uint16_t (&buf)[2][2 * SUB]) {
-      if (!active || !((sg.mask >> member) & 1)) return;
-      f32x16 s0;
-      bf16x8 v0[2 * NM];
-      qk(&buf[0][0], &buf[1][0], s0, v0);
-      max_rescale(s0, sg.nk);
-      bf16x8 p00, p01;
-      if (sg.ns == 2) {
-        f32x16 s1;
-        bf16x8 v1[2 * NM];
-        expp(s0, p00, p01);
-        qk(&buf[0][SUB], &buf[1][SUB], s1, v1);
-        pv(v0, p00, p01);
-        max_rescale(s1, sg.nk - 32);
-        bf16x8 p10, p11;
-        expp(s1, p10, p11);
-        pv(v1, p10, p11);
-      } else {
-        expp(s0, p00, p01);
-        pv(v0, p00, p01);
-      }
-    };
-
-    // ---- two buffer pairs: one pair of stages is computed while the next
-    // pair is copied; one barrier per pair of stages ----
+    // ---- stage ring of four slots: stage s is computed from slot s % 4
+    // while stages s+1 and s+2 are in flight; one barrier per stage ----
     Stage none;
     none.pos = -1; none.j = 0; none.n = 0; none.s0 = 0; none.ns = 0; none.nk = 0; none.mask = 0;
     Stage cur = next_stage(g, ulist, ublkn, ucnt, none);
     if (cur.pos >= 0) {
-      Stage s1 = next_stage(g, ulist, ublkn, ucnt, cur);
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-      issue(cur, kv0);
-      if (s1.pos >= 0) issue(s1, kv1);
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-      __builtin_amdgcn_s_barrier();
-      auto superstep = [&](uint16_t (&ca)[2][2 * SUB], uint16_t (&cb)[2][2 * SUB], uint16_t (&na)[2][2 * SUB],
-                           uint16_t (&nb)[2][2 * SUB]) -> bool {
-        const Stage s2 = s1.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, s1) : none;
-        const Stage s3 = s2.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, s2) : none;
-        if (s2.pos >= 0) issue(s2, na);
-        if (s3.pos >= 0) issue(s3, nb);
-        compute(cur, ca);
-        if (s1.pos >= 0) compute(s1, cb);
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-        __builtin_amdgcn_s_barrier();
-        cur = s2;
-        s1 = s3;
-        return cur.pos >= 0;
-      };
+      Stage nxt = next_stage(g, ulist, ublkn, ucnt, cur);
+      Stage nn = nxt.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, nxt) : none;
+      issue(cur, 0);
+      if (nxt.pos >= 0) issue(nxt, 1);
+      if (nn.pos >= 0) issue(nn, 2);
+      bool did_prev = true;  // no LDS reads of this unit are outstanding yet
+      int slot = 0;
       for (;;) {
-        if (!superstep(kv0, kv1, kv2, kv3)) break;
-        if (!superstep(kv2, kv3, kv0, kv1)) break;
+        // own copies of this stage have landed (those of the next two may
+        // still fly); a wave that skipped the previous stage may still have
+        // reads of the slot about to be refilled outstanding
+        if (nn.pos >= 0) {
+          if (did_prev) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * PER));
+          else __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * PER) & ~(15 << 8));
+        } else if (nxt.pos >= 0) {
+          if (did_prev) __builtin_amdgcn_s_waitcnt(vm_wait_imm(PER));
+          else __builtin_amdgcn_s_waitcnt(vm_wait_imm(PER) & ~(15 << 8));
+        } else {
+          if (did_prev) __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+          else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0) & ~(15 << 8));
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        did_prev = active && ((cur.mask >> member) & 1);
+        if (did_prev) {
+          const int kb = slot * 4 * SUB;
+#pragma unroll 1
+          for (int t = 0; t < cur.ns; ++t) step(min(32, cur.nk - 32 * t), kb + t * SUB, kb + 2 * SUB + t * SUB);
+        }
+        // stage s+3 goes into the slot of stage s-1, which every wave left
+        // before the barrier above
+        const Stage n3 = nn.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, nn) : none;
+        if (n3.pos >= 0) issue(n3, (slot + 3) & 3);
+        cur = nxt;
+        nxt = nn;
+        nn = n3;
+        slot = (slot + 1) & 3;
+        if (cur.pos < 0) break;
       }
     }
 
@@ -570,7 +611,7 @@ hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpac
   queue_kernel<<<1, kQThreads, 0, s>>>(g, U, row_ptr, col_capacity, queue);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int grid = num_cus;  // one 8-wave workgroup per CU (LDS-limited)
+  int grid = num_cus;  // one 12-wave workgroup per CU (LDS-limited)
   if (grid > U) grid = U;
   if (grid < 1) grid = 1;
   const float scale_log2 = scale * 1.4426950408889634f;
