@@ -147,6 +147,17 @@ TEST_CONFIGS = {
     "d64": Config("d64", B=1, H=2, d=64, T=6, Hh=10, W=16, bt=3, bh=5, bw=8,
                   dtype="bf16", sigma=0.5, amp_kind="uniform", amp_params=(0.3, 2.0),
                   mode=MODE_MASS, budget=(0.8,), seed=18),
+    # the supported limits: 4096 blocks per head (one token each), a block
+    # count between 2048 and 4096, and 1024-token blocks.
+    "max_blocks": Config("max_blocks", B=1, H=1, d=64, T=16, Hh=16, W=16, bt=1, bh=1, bw=1,
+                         dtype="bf16", sigma=0.5, amp_kind="const", amp_params=(1.0,),
+                         mode=MODE_COUNT, budget=(8,), seed=20),
+    "blocks_2k": Config("blocks_2k", B=1, H=1, d=128, T=12, Hh=12, W=12, bt=1, bh=1, bw=1,
+                        dtype="bf16", sigma=0.5, amp_kind="const", amp_params=(1.0,),
+                        mode=MODE_MASS, budget=(0.3,), seed=21),
+    "max_block_tokens": Config("max_block_tokens", B=1, H=1, d=128, T=8, Hh=32, W=32, bt=4, bh=16, bw=16,
+                               dtype="bf16", sigma=0.5, amp_kind="const", amp_params=(1.0,),
+                               mode=MODE_COUNT, budget=(3,), seed=22),
     # fp32 (debug) path on a ragged shape.
     "ragged_f32": Config("ragged_f32", B=1, H=2, d=128, T=5, Hh=7, W=9, bt=4, bh=4, bw=4,
                          dtype="f32", sigma=1.0, amp_kind="const", amp_params=(0.0,),

@@ -300,6 +300,36 @@ def test_attention_matches_oracle(name):
     assert compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), name) == 0
 
 
+# the supported limits: 4096 and 1728 blocks per head (the widest selection
+# rows), and 1024-token blocks (eight 128-query tiles per row, 32 key subtiles
+# per block)
+LIMITS = ["max_blocks", "blocks_2k", "max_block_tokens"]
+
+
+@pytest.mark.parametrize("name", LIMITS)
+def test_limits_selection_and_attention_match_oracle(name):
+    cfg = synth.get_config(name)
+    print(f"[limits] {name}", flush=True)
+    x = synth.make_inputs(cfg)
+    g = geom(cfg)
+    grid, block = grid_block(cfg)
+    qd, kd = to_dev(cfg, x["q"]), to_dev(cfg, x["k"])
+    qm, km = spade.summarize(qd, kd, grid, block)
+    scale = oracle.default_scale(cfg.d)
+    qm_ref, km_ref = oracle_means(cfg, x["q"]), oracle_means(cfg, x["k"])
+    assert np.array_equal(qm.cpu().numpy().astype(np.float64), qm_ref)
+    assert np.array_equal(km.cpu().numpy().astype(np.float64), km_ref)
+    S_ref = oracle.estimate(qm_ref, km_ref, scale)
+    sel = oracle.select(S_ref, cfg.mode, cfg.per_head_budget())
+    o, rp, ci = run_attn(cfg, x)
+    rp, ci = csr_rows(rp, ci)
+    assert compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), name) == 0
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], g, rp, ci, scale)
+    err = np.abs(dev_to_f64(o) - ref).max()
+    assert err <= BF16_TOL, err
+
+
 @pytest.mark.parametrize("name", ["ragged_small", "ragged_p64", "tiny", "ragged_f32"])
 def test_ratio_one_equals_dense_attention(name):
     cfg = synth.get_config(name)
