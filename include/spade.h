@@ -25,8 +25,12 @@
  * - Pointers named q, k, v, o, q_mean, k_mean, row_ptr, col_idx, scores and
  *   workspace are DEVICE pointers owned by the caller.  spade_problem and
  *   spade_budget (and budget->per_head) are HOST memory read during the call.
- *   The library never allocates or frees device memory and keeps no state
- *   other than a per-device cache of the compute-unit count.
+ *   The library never allocates or frees device memory.  Its only state is
+ *   a per-device cache of the compute-unit count and the per-thread events of
+ *   spade_profile_events.
+ * - The workspace holds per-call scratch (summaries, scores, packed operand
+ *   tiles, the attention work queues): calls that may run at the same time,
+ *   on one stream or several, each need a workspace of their own.
  * - Every compute call validates its arguments on the host first; on any
  *   error it returns a status and launches nothing.  Launches are
  *   asynchronous on `stream` (a hipStream_t; NULL = the default stream); the
