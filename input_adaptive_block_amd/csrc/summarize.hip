@@ -31,6 +31,8 @@
 //         V[key 32 s + 16 kc + 8 (e/4) + 4 (L/32) + e%4][32 m + L%32],
 //         which is the A operand of O^T += V^T P^T for the key order in which
 //         the S^T accumulator of v_mfma_f32_32x32x16_bf16 leaves P.
+#include <type_traits>
+
 #include "spade_internal.h"
 
 namespace spade {
@@ -73,6 +75,10 @@ __device__ inline double group_sum(double x) {
 // The Summarizer's reduction: sum (mean), maximum or minimum.
 __device__ inline double sum_op(int op, double a, double b) {
   return op == 0 ? a + b : (op == 1 ? fmax(a, b) : fmin(a, b));
+}
+template <int OP>
+__device__ inline double sum_op_t(double a, double b) {
+  return OP == 0 ? a + b : (OP == 1 ? fmax(a, b) : fmin(a, b));
 }
 __device__ inline double sum_identity(int op) {
   return op == 0 ? 0.0 : (op == 1 ? -__builtin_huge_val() : __builtin_huge_val());
@@ -130,56 +136,64 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
   }
 
   if (role < 2 || !PACK) {
-    uint16_t* pk = nullptr;
-    if (PACK) pk = (role == 0 ? qpack : kpack) + ((size_t)bh * g.nblk + j) * (size_t)g.P * D;
-    const int rows = PACK ? g.P : box.n;
-    for (int l = lrow; l < rows; l += TPP) {
-      Vec16 x = {{0u, 0u, 0u, 0u}};
-      if (l < box.n) {
-        const int tok = block_token(g, box, l);
-        x = *reinterpret_cast<const Vec16*>(src + (head_base + (size_t)tok * D + c0) * elem);
-      }
-      if (want_mean || want_sics) {
-        double xe[EPV];
-        if (BF16) {
+    // the token loop, compiled once per reduction so each keeps only its own
+    // fp64 arithmetic
+    auto token_loop = [&](auto op_c) __attribute__((always_inline)) {
+      constexpr int OP = decltype(op_c)::value;
+      uint16_t* pk = nullptr;
+      if (PACK) pk = (role == 0 ? qpack : kpack) + ((size_t)bh * g.nblk + j) * (size_t)g.P * D;
+      const int rows = PACK ? g.P : box.n;
+      for (int l = lrow; l < rows; l += TPP) {
+        Vec16 x = {{0u, 0u, 0u, 0u}};
+        if (l < box.n) {
+          const int tok = block_token(g, box, l);
+          x = *reinterpret_cast<const Vec16*>(src + (head_base + (size_t)tok * D + c0) * elem);
+        }
+        if (want_mean || want_sics) {
+          double xe[EPV];
+          if (BF16) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xe[2 * e] = (double)bf16_lo(x.w[e]);
-            xe[2 * e + 1] = (double)bf16_hi(x.w[e]);
+            for (int e = 0; e < 4; ++e) {
+              xe[2 * e] = (double)bf16_lo(x.w[e]);
+              xe[2 * e + 1] = (double)bf16_hi(x.w[e]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xe[e] = (double)__uint_as_float(x.w[e]);
           }
-        } else {
+          if (l < box.n) {  // padded rows (zeros) take no part in a max or min
 #pragma unroll
-          for (int e = 0; e < 4; ++e) xe[e] = (double)__uint_as_float(x.w[e]);
-        }
-        if (l < box.n) {  // padded rows (zeros) take no part in a max or min
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) acc[e] = sum_op(op, acc[e], xe[e]);
-        }
-        if (want_sics) {
-          // squared norm of the token over its TPT threads (consecutive lanes;
-          // every thread of the group runs the same iterations)
-          double ss = 0.0;
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) ss += xe[e] * xe[e];
-          ss = group_sum<TPT>(ss);
-          // 1/|x|: fp32 reciprocal square root refined by one Newton step in
-          // fp64 (relative error ~1e-14, far below the fp32 result's ulp)
-          double inv = 0.0;
-          if (ss > 0.0) {
-            const double r = (double)__builtin_amdgcn_rsqf((float)ss);
-            inv = r * (1.5 - 0.5 * ss * r * r);
+            for (int e = 0; e < EPV; ++e) acc[e] = sum_op_t<OP>(acc[e], xe[e]);
           }
+          if (want_sics) {
+            // squared norm of the token over its TPT threads (consecutive lanes;
+            // every thread of the group runs the same iterations)
+            double ss = 0.0;
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) uacc[e] += xe[e] * inv;
+            for (int e = 0; e < EPV; ++e) ss += xe[e] * xe[e];
+            ss = group_sum<TPT>(ss);
+            // 1/|x|: fp32 reciprocal square root refined by one Newton step in
+            // fp64 (relative error ~1e-14, far below the fp32 result's ulp)
+            double inv = 0.0;
+            if (ss > 0.0) {
+              const double r = (double)__builtin_amdgcn_rsqf((float)ss);
+              inv = r * (1.5 - 0.5 * ss * r * r);
+            }
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) uacc[e] += xe[e] * inv;
+          }
+        }
+        if (PACK) {
+          const int sub = l >> 5, kl = l & 31;
+          const int c = c0 >> 4, half = (c0 >> 3) & 1;
+          const size_t dst = ((size_t)(sub * (D / 16) + c) * 64 + kl + 32 * half) * 8;
+          *reinterpret_cast<Vec16*>(pk + dst) = x;
         }
       }
-      if (PACK) {
-        const int sub = l >> 5, kl = l & 31;
-        const int c = c0 >> 4, half = (c0 >> 3) & 1;
-        const size_t dst = ((size_t)(sub * (D / 16) + c) * 64 + kl + 32 * half) * 8;
-        *reinterpret_cast<Vec16*>(pk + dst) = x;
-      }
-    }
+    };
+    if (op == 0) token_loop(std::integral_constant<int, 0>{});
+    else if (op == 1) token_loop(std::integral_constant<int, 1>{});
+    else token_loop(std::integral_constant<int, 2>{});
   } else {
     // V: transpose through LDS, 128 tokens (four 32-key subtiles) at a time.
     uint16_t* pk = vpack + ((size_t)bh * g.nblk + j) * (size_t)g.P * D;
