@@ -576,6 +576,37 @@ def test_attn_schemes_matches_oracle_and_single_scheme_runs(name):
     assert np.abs(of[same] - ref[same]).max() <= tol
 
 
+@pytest.mark.parametrize("name,window,summarizer", [("mid_shape", (1, 1, 1), "max"), ("ragged_small", (0, 1, 0), "mean"),
+                                                     ("tiny", (1, 0, 0), "min")])
+def test_attn_schemes_with_window_and_summarizer(name, window, summarizer):
+    """The three extensions together: head-wise schemes whose per-candidate
+    paths use a static window and a max/min summarizer; every head equals its
+    single-scheme run bit for bit and the oracle's head-wise path."""
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    cands = candidates_for(cfg)
+    grid = (cfg.T, cfg.Hh, cfg.W)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    bud = cfg.per_head_budget()
+    o, scheme, agg = spade.attn_schemes(q, k, v, grid, cands, cfg.mode, bud, summarizer=summarizer,
+                                        window=window)
+    torch.cuda.synchronize()
+    sch = scheme.cpu().numpy()
+    for c, blk in enumerate(cands):
+        oc, _, _ = spade.attn(q, k, v, grid, blk, cfg.mode, bud, summarizer=summarizer, window=window)
+        m = torch.from_numpy(sch == c).cuda()
+        assert torch.equal(o[m], oc[m]), f"{name}: heads of candidate {c}"
+    ref, choice, _ = oracle.spade_attn_schemes(*(to_f64(cfg, x[n]) for n in ("q", "k", "v")), cfg.T, cfg.Hh,
+                                               cfg.W, cands, cfg.mode, bud, summarizer=summarizer,
+                                               window=window)
+    _, margin = oracle.choose_scheme(oracle.scheme_aggregate(to_f64(cfg, x["q"]), to_f64(cfg, x["k"]),
+                                                             cfg.T, cfg.Hh, cfg.W, cands))
+    same = (sch == choice)
+    assert (same | (margin <= 1e-9)).all()
+    tol = BF16_TOL if cfg.dtype == "bf16" else F32_TOL
+    assert np.abs(dev_to_f64(o)[same] - ref[same]).max() <= tol
+
+
 def test_single_candidate_equals_the_plain_path():
     cfg = synth.get_config("mid_shape")
     x = synth.make_inputs(cfg)
