@@ -533,6 +533,26 @@ def test_scheme_select_matches_oracle(name):
     assert ((got == choice) | (margin <= 1e-9)).all()
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["mid", "ragged"])
+def test_full_size_scheme_select(name):
+    """Scheme selection over the three blocking candidates bench.py times, at
+    the full workload: every (b, h) aggregate and choice against the oracle."""
+    cfg = synth.get_config(name)
+    print(f"[full schemes] {name}", flush=True)
+    x = synth.make_inputs(cfg)
+    cands = candidates_for(cfg)
+    qd, kd = to_dev(cfg, x["q"]), to_dev(cfg, x["k"])
+    agg, scheme = spade.scheme_select(qd, kd, (cfg.T, cfg.Hh, cfg.W), cands)
+    ref = oracle.scheme_aggregate(to_f64(cfg, x["q"]), to_f64(cfg, x["k"]), cfg.T, cfg.Hh, cfg.W, cands)
+    np.testing.assert_allclose(agg.cpu().numpy().astype(np.float64), ref, rtol=1e-6, atol=1e-9)
+    choice, margin = oracle.choose_scheme(ref)
+    got = scheme.cpu().numpy()
+    assert ((got == choice) | (margin <= 1e-9)).all()
+    print(f"[full schemes] {name}: choices {np.bincount(got.ravel(), minlength=len(cands))}, "
+          f"min margin {margin.min():.2e}", flush=True)
+
+
 def test_scheme_choice_follows_constructed_fields():
     """Tokens constant along time pick the temporal blocking; tokens constant
     within each frame pick the spatial one (aggregate 1 exactly)."""
