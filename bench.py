@@ -292,7 +292,9 @@ def main():
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": traffic,
         },
-        "device": torch.cuda.get_device_name(0),
+        "device": "%s (%s, %d CUs)" % (torch.cuda.get_device_name(0),
+                                       getattr(torch.cuda.get_device_properties(0), "gcnArchName", "?"),
+                                       torch.cuda.get_device_properties(0).multi_processor_count),
         "hip": torch.version.hip,
         "context": ("the pages report 2.26x-3.40x attention speedup over FlashAttention-3 on an NVIDIA "
                     "H800 for 720p video models; no absolute figure exists to compare with"),
