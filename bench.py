@@ -146,9 +146,8 @@ def main():
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the heads shard across GPUs "
-                                   "without communication inside the method (see the design notes), "
-                                   "but no multi-GPU path is built", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "one GPU only: the heads shard across GPUs without communication "
+                                   "inside the method, but no multi-GPU path exists", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np

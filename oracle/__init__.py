@@ -1,6 +1,6 @@
 """CPU oracle of the block-sparse attention path: test infrastructure only.
 
-Imported only by tests/, the graft smoke check and the bench's CPU-baseline
+Imported only by tests/, __graft_entry__.smoke() and the bench's CPU-baseline
 leg.  It shares no code with the HIP library.
 """
 from .spade_oracle import *  # noqa: F401,F403

@@ -1,7 +1,7 @@
 """CPU oracle for SPADE's executor hot path (test infrastructure only).
 
 This module is the plain, slow, obviously-correct statement of what the
-block-sparse attention path computes.  Only the tests, the graft smoke check
+block-sparse attention path computes.  Only the tests, __graft_entry__.smoke()
 and the bench's CPU-baseline leg may import it; the product library never
 does, and the two share no code.
 
@@ -14,7 +14,7 @@ Block-Sparse Attention), plus the abstract on the catalyzex author pages
 (executor with index search and flash block-sparse attention).
 
 Arithmetic is fp64 unless a step states otherwise.  Readings taken where the
-pages are silent (each also listed in the design notes):
+pages are silent:
 
 * tokens are flattened in raster order n = (t*Hh + h)*W + w;
 * blocks tile the grid from the origin with stride (bt, bh, bw); the last
