@@ -230,6 +230,17 @@ void spade_profile_events(void* start, void* stop);
 spade_status spade_debug_scores(const spade_problem* p, const float* q_mean, const float* k_mean,
                                 double* scores, void* stream);
 
+/* Test hook: the work queues the bf16 attention kernel would take for this
+ * CSR.  queue (device, int32[18]) receives the first unit of each of the 8
+ * queues and the end (U, the number of units), then 8 cursors set to 0;
+ * the last entry is left untouched.
+ * Units are the (row, 32-query subtile) items of a head in order, 12 at a
+ * time; a unit costs 1 + the kept blocks of each of its items' rows, and
+ * queue x starts at the first unit whose exclusive cost prefix reaches
+ * ceil(x * total / 8).  Summarizes and packs nothing. */
+spade_status spade_debug_work_queues(const spade_problem* p, const int32_t* row_ptr, int64_t col_capacity,
+                                     int32_t* queue, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,7 @@ from ._lib import (  # noqa: F401
     SPADE_SUM_MAX, SPADE_SUM_MEAN, SPADE_SUM_MIN,
     SPADE_KEEP_COUNT, SPADE_KEEP_MASS, SPADE_KEEP_RATIO, SPADE_OK, SPADE_ERR_CAPACITY,
     SPADE_ERR_DEVICE, SPADE_ERR_INVALID_ARG, SPADE_ERR_UNSUPPORTED, lib, spade_attn,
-    spade_block_sparse_attn, spade_check, spade_debug_scores, spade_estimate_select,
+    spade_block_sparse_attn, spade_check, spade_debug_scores, spade_debug_work_queues, spade_estimate_select,
     spade_attn_schemes, spade_max_nnz, spade_num_blocks, spade_profile_events, spade_scheme_select,
     spade_schemes_workspace_bytes, spade_summarize, spade_summarize_sics,
     spade_workspace_bytes,
@@ -26,7 +26,7 @@ __all__ = [
     "block_sparse_attn", "attn", "debug_scores", "alloc_workspace", "scheme_select", "attn_schemes",
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
     "spade_summarize", "spade_summarize_sics", "spade_estimate_select", "spade_block_sparse_attn", "spade_attn",
-    "spade_debug_scores", "spade_schemes_workspace_bytes", "spade_scheme_select", "spade_attn_schemes",
+    "spade_debug_scores", "spade_debug_work_queues", "spade_schemes_workspace_bytes", "spade_scheme_select", "spade_attn_schemes",
 ]
 
 

@@ -134,6 +134,7 @@ def _load() -> ctypes.CDLL:
         "spade_block_sparse_attn": (st, [P, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
         "spade_attn": (st, [P, vp, vp, vp, Bp, vp, vp, vp, i64, vp, sz, vp]),
         "spade_debug_scores": (st, [P, vp, vp, vp, vp]),
+        "spade_debug_work_queues": (st, [P, vp, i64, vp, vp]),
         "spade_schemes_workspace_bytes": (sz, [P, vp, ctypes.c_int32, Bp]),
         "spade_scheme_select": (st, [P, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]),
         "spade_attn_schemes": (st, [P, vp, vp, vp, vp, ctypes.c_int32, Bp, vp, vp, vp, vp, sz, vp]),
@@ -151,7 +152,8 @@ _LIB = _load()
 EXPORTED = (
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
     "spade_status_string", "spade_summarize", "spade_summarize_sics", "spade_estimate_select",
-    "spade_block_sparse_attn", "spade_attn", "spade_debug_scores", "spade_profile_events",
+    "spade_block_sparse_attn", "spade_attn", "spade_debug_scores", "spade_debug_work_queues",
+    "spade_profile_events",
     "spade_schemes_workspace_bytes", "spade_scheme_select", "spade_attn_schemes",
 )
 
@@ -244,6 +246,11 @@ def spade_attn(problem: Problem, q, k, v, budget: Budget, o, row_ptr, col_idx, c
 def spade_debug_scores(problem: Problem, q_mean, k_mean, scores, stream=None) -> None:
     _check(_LIB.spade_debug_scores(ctypes.byref(problem.c()), _ptr(q_mean), _ptr(k_mean), _ptr(scores),
                                    _stream(stream)), "spade_debug_scores")
+
+
+def spade_debug_work_queues(problem: Problem, row_ptr, col_capacity: int, queue, stream=None) -> None:
+    _check(_LIB.spade_debug_work_queues(ctypes.byref(problem.c()), _ptr(row_ptr), int(col_capacity), _ptr(queue),
+                                        _stream(stream)), "spade_debug_work_queues")
 
 
 def spade_profile_events(start, stop) -> None:

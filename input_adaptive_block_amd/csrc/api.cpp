@@ -381,6 +381,16 @@ spade_status spade_debug_scores(const spade_problem* p, const float* q_mean, con
   return dev(launch_scores(g, q_mean, k_mean, est_scale(p), scores, (hipStream_t)stream));
 }
 
+spade_status spade_debug_work_queues(const spade_problem* p, const int32_t* row_ptr, int64_t col_capacity,
+                                     int32_t* queue, void* stream) {
+  Geom g;
+  SPADE_TRY(make_geom(p, &g));
+  if (col_capacity < 0) return SPADE_ERR_INVALID_ARG;
+  if (g.R == 0) return SPADE_OK;
+  if (!row_ptr || !queue) return SPADE_ERR_INVALID_ARG;
+  return dev(launch_work_queues(g, row_ptr, col_capacity, queue, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

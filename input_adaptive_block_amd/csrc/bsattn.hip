@@ -7,13 +7,15 @@
 // launch to raise occupancy ("Head Grouping").  The pages' kernel targets
 // Hopper (TMA, warp-group MMA); this one is written for CDNA4:
 //
-// * Work unit = three consecutive (row, 128-query tile) items of one head --
-//   neighbouring Q blocks, whose kept KV sets overlap heavily.  The unit
-//   streams the UNION of their kept blocks once (ascending block id); each
-//   third of the workgroup (4 wavefronts x 32 queries) computes only on the
-//   blocks its own row keeps.  A K/V byte fetched once serves every tile of
-//   the unit that keeps its block, which cuts L2 / Infinity-Cache traffic on
-//   video layers, where neighbouring rows keep mostly the same blocks.
+// * Work unit = twelve consecutive (row, 32-query subtile) items of one head,
+//   one per wavefront: three rows of 120-token blocks, six of 64-token blocks,
+//   up to twelve of small ones -- neighbouring Q blocks, whose kept KV sets
+//   overlap heavily.  The unit streams the UNION of its rows' kept blocks once
+//   (ascending block id, each entry with the mask of the rows keeping it);
+//   each wavefront computes only on the blocks its own row keeps.  A K/V byte
+//   fetched once serves every row of the unit that keeps its block, which
+//   cuts L2 / Infinity-Cache traffic on video layers, where neighbouring rows
+//   keep mostly the same blocks.
 // * One persistent workgroup of 12 wavefronts per CU (three per SIMD) pulls
 //   units from eight contiguous queues (one per XCD, equal shares of kept
 //   blocks); a workgroup starts on queue blockIdx % 8 and steals from the next
@@ -57,27 +59,28 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kMembers = 3;                       // query tiles per work unit
 constexpr int kCopyWaves = 8;                     // waves that issue the stage copies
-constexpr int kWavesPerMember = 4;                // 4 x 32 queries = one 128-query tile
-constexpr int kWaves = kMembers * kWavesPerMember;
+constexpr int kWaves = 12;                        // one 32-query item per wave
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQTile = 32 * kWavesPerMember;
+constexpr int kMaxUnitRows = kWaves;              // rows a unit's items can span
 constexpr float kLazy = 8.0f;                     // log2 headroom before a rescale
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-// Work units: the (row, q-tile) items of one head in order, kMembers at a time.
+// Work units: the (row, 32-query subtile) items of one head in order, one
+// per wave, kWaves at a time.  A unit spans ceil(kWaves / nsub) rows or so
+// (three rows of 120-token blocks, six of 64-token blocks), never more than
+// kMaxUnitRows.
 struct UnitMap {
-  int nqt;         // q-tiles per row
-  int items;       // items per head = nblk * nqt
-  int per_head;    // units per head = ceil(items / kMembers)
+  int nsub;        // 32-query subtiles per row (P / 32)
+  int items;       // items per head = nblk * nsub
+  int per_head;    // units per head = ceil(items / kWaves)
 };
 
 __host__ __device__ inline UnitMap unit_map(const Geom& g) {
   UnitMap u;
-  u.nqt = (g.P + kQTile - 1) / kQTile;
-  u.items = g.nblk * u.nqt;
-  u.per_head = (u.items + kMembers - 1) / kMembers;
+  u.nsub = g.P / 32;
+  u.items = g.nblk * u.nsub;
+  u.per_head = (u.items + kWaves - 1) / kWaves;
   return u;
 }
 
@@ -102,13 +105,13 @@ __global__ __launch_bounds__(kQThreads) void queue_kernel(Geom g, int U, const i
   if (tid <= kQueues) start[tid] = (tid == 0) ? 0 : U;
   const int per = (U + kQThreads - 1) / kQThreads;
   const int lo = min(U, tid * per), hi = min(U, lo + per);
-  // cost of a unit: kept blocks of its rows (a bound on its union) + 1
+  // cost of a unit: kept blocks of each wave's row + 1
   auto cost = [&](int u) -> long long {
     const int bh = u / um.per_head, pi = u - bh * um.per_head;
     long long c = 1;
-    for (int m = 0; m < kMembers; ++m) {
-      const int it = kMembers * pi + m;
-      if (it < um.items) c += row_cost(row_ptr, cap, bh * g.nblk + it / um.nqt);
+    for (int w = 0; w < kWaves; ++w) {
+      const int it = kWaves * pi + w;
+      if (it < um.items) c += row_cost(row_ptr, cap, bh * g.nblk + it / um.nsub);
     }
     return c;
   };
@@ -124,12 +127,15 @@ __global__ __launch_bounds__(kQThreads) void queue_kernel(Geom g, int U, const i
   }
   const long long total = part[kQThreads - 1];
   long long run = part[tid] - s;  // exclusive prefix before unit lo
-  long long prev = run;
+  // exclusive prefix before the previous unit (-1 before unit 0)
+  long long prev = lo > 0 && lo < hi ? run - cost(lo - 1) : -1;
   for (int u = lo; u < hi; ++u) {
-    // start[x] = first unit whose exclusive prefix reaches ceil(x * total / 8)
+    // start[x] = first unit whose exclusive prefix reaches ceil(x * total / 8);
+    // exactly one unit satisfies this for each x, so the starts are ascending
+    // and the queues partition the units
     for (int x = 1; x < kQueues; ++x) {
       const long long t = (x * total + kQueues - 1) / kQueues;
-      if (run >= t && (u == 0 || prev < t)) start[x] = u;
+      if (run >= t && prev < t) start[x] = u;
     }
     prev = run;
     run += cost(u);
@@ -144,7 +150,8 @@ __global__ __launch_bounds__(kQThreads) void queue_kernel(Geom g, int U, const i
 // ---------------------------------------------------------------------------
 
 // Position in the unit's union list: block j (entry pos), subtiles
-// [s0, s0 + ns) of it, nk valid keys from subtile s0 on, member bit mask.
+// [s0, s0 + ns) of it, nk valid keys from subtile s0 on, mask of the unit's
+// rows that keep the block.
 struct Stage {
   int pos;  // -1: no stage
   int j;
@@ -155,7 +162,7 @@ struct Stage {
   int mask;
 };
 
-__device__ inline Stage next_stage(const Geom& g, const uint16_t* ul, const uint16_t* un, int cnt,
+__device__ inline Stage next_stage(const Geom& g, const uint32_t* ul, const uint16_t* un, int cnt,
                                   const Stage& cur) {
   Stage st = cur;
   if (cur.pos >= 0) {
@@ -174,7 +181,7 @@ __device__ inline Stage next_stage(const Geom& g, const uint16_t* ul, const uint
   }
   const int e = __builtin_amdgcn_readfirstlane((int)ul[st.pos]);
   st.j = e & 0xFFF;
-  st.mask = e >> 12;
+  st.mask = (int)((unsigned)e >> 12);
   st.n = __builtin_amdgcn_readfirstlane((int)un[st.pos]);
   st.s0 = 0;
   st.ns = min(2, (st.n + 31) >> 5);
@@ -202,18 +209,20 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
   // four stage slots; the copies into them are issued from inline asm, so the
   // compiler does not order the slot being read behind the copies in flight
   __shared__ __attribute__((aligned(1024))) uint16_t ring[4 * 2 * 2 * SUB];  // [slot][K,V][2 subtiles]
-  __shared__ uint8_t flags[kMembers][kMaxBlocks];
-  __shared__ uint16_t ulist[kMaxBlocks];
+  // union list entries: block id | mask of the unit's rows keeping it << 12
+  __shared__ uint32_t ulist[kMaxBlocks];
   __shared__ uint16_t ublkn[kMaxBlocks];  // tokens of each union entry's block
+  // per-block row masks while the union is built (two blocks per word), in
+  // the ring, which holds no stage between units
+  uint32_t* const rowbits = reinterpret_cast<uint32_t*>(ring);
+  static_assert(kMaxBlocks / 2 * 4 <= 4 * 2 * 2 * SUB * 2, "row masks fit in the ring");
   __shared__ int scanbuf[kThreads];
   __shared__ int s_unit;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: member tests stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: row-mask tests stay scalar
   const int half = lane >> 5;
-  const int member = wave / kWavesPerMember;
-  const int lw = wave - member * kWavesPerMember;
   const UnitMap um = unit_map(g);
   const int* qstart = queue;
   int* qcursor = queue + kQueues + 1;
@@ -248,30 +257,29 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
       continue;
     }
 
-    // ---- the unit's union list of kept blocks, with member masks ----
-    for (int t = tid; t < g.nblk; t += kThreads) {
-#pragma unroll
-      for (int m = 0; m < kMembers; ++m) flags[m][t] = 0;
-    }
+    // ---- the unit's union list of kept blocks, with row masks ----
+    const int it0 = kWaves * pi;
+    const int it_last = min(um.items, it0 + kWaves) - 1;
+    const int row0 = it0 / um.nsub;
+    const int nrows = it_last / um.nsub - row0 + 1;  // 1 .. kMaxUnitRows
+    for (int t = tid; t < (g.nblk + 1) / 2; t += kThreads) rowbits[t] = 0u;
     __syncthreads();
-#pragma unroll
-    for (int m = 0; m < kMembers; ++m) {
-      const int it = kMembers * pi + m;
-      if (it >= um.items) continue;
-      const int r = bh * g.nblk + it / um.nqt;
+    for (int m = 0; m < nrows; ++m) {
+      const int r = bh * g.nblk + row0 + m;
       long long a = row_ptr[r], b = row_ptr[r + 1];
       a = a < 0 ? 0 : (a > cap ? cap : a);
       b = b < a ? a : (b > cap ? cap : b);
       for (long long e = a + tid; e < b; e += kThreads) {
         const int j = col_idx[e];
-        if (j >= 0 && j < g.nblk) flags[m][j] = 1;
+        if (j >= 0 && j < g.nblk) atomicOr(&rowbits[j >> 1], (1u << m) << (16 * (j & 1)));
       }
     }
     __syncthreads();
+    auto row_mask = [&](int j) __attribute__((always_inline)) { return (rowbits[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
     const int per = (g.nblk + kThreads - 1) / kThreads;
     const int jb = min(g.nblk, tid * per), je = min(g.nblk, jb + per);
     int cnt = 0;
-    for (int j = jb; j < je; ++j) cnt += (flags[0][j] | flags[1][j] | flags[2][j]) != 0;
+    for (int j = jb; j < je; ++j) cnt += row_mask(j) != 0u;
     scanbuf[tid] = cnt;
     __syncthreads();
     for (int off = 1; off < kThreads; off <<= 1) {
@@ -283,23 +291,23 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     {
       int w = scanbuf[tid] - cnt;
       for (int j = jb; j < je; ++j) {
-        const int msk = flags[0][j] | (flags[1][j] << 1) | (flags[2][j] << 2);
+        const uint32_t msk = row_mask(j);
         if (msk) {
           ublkn[w] = (uint16_t)block_box(g, j).n;
-          ulist[w++] = (uint16_t)(j | (msk << 12));
+          ulist[w++] = (uint32_t)j | (msk << 12);
         }
       }
     }
     const int ucnt = scanbuf[kThreads - 1];
-    __syncthreads();
+    __syncthreads();  // the ring is free again for the stage copies
 
     // ---- this wave's 32 queries ----
-    const int my_it = kMembers * pi + member;
+    const int my_it = it0 + wave;
     const bool has_item = my_it < um.items;
-    const int my_i = has_item ? my_it / um.nqt : 0;
-    const int my_qt = has_item ? my_it - my_i * um.nqt : 0;
+    const int my_i = has_item ? my_it / um.nsub : row0;
+    const int qsub = has_item ? my_it - my_i * um.nsub : 0;
+    const int my_row = my_i - row0;  // this wave's bit in the union masks
     const BlockBox qbox = block_box(g, my_i);
-    const int qsub = my_qt * kWavesPerMember + lw;
     const bool active = has_item && 32 * qsub < qbox.n;
     bf16x8 qop[NC];
     if (active) {
@@ -471,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        did_prev = active && ((cur.mask >> member) & 1);
+        did_prev = active && ((cur.mask >> my_row) & 1);
         if (did_prev) {
           const int kb = slot * 4 * SUB;
 #pragma unroll 1
@@ -510,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
           }
       }
     }
-    __syncthreads();  // s_unit, flags and ulist are reused by the next unit
+    __syncthreads();  // s_unit, the ring and ulist are reused by the next unit
   }
 }
 
@@ -601,6 +609,14 @@ __global__ __launch_bounds__(kF32Threads) void bsattn_f32_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_work_queues(const Geom& g, const int* row_ptr, long long col_capacity, int* queue,
+                              hipStream_t s) {
+  if (g.R == 0) return hipSuccess;
+  const int U = g.BH * unit_map(g).per_head;
+  queue_kernel<<<1, kQThreads, 0, s>>>(g, U, row_ptr, col_capacity, queue);
+  return hipGetLastError();
+}
 
 hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpack, const void* vpack,
                               const int* row_ptr, const int* col_idx, long long col_capacity, float scale,

@@ -112,6 +112,10 @@ hipError_t launch_select(const Geom& g, const double* scores, const SelectArgs& 
 hipError_t launch_scan(const Geom& g, const int* counts, int* row_ptr, hipStream_t s);
 hipError_t launch_compact(const Geom& g, const int* row_ptr, const uint32_t* mask, int mask_words,
                           int* col_idx, hipStream_t s);
+// The attention kernel's work queues for a CSR (start of each queue's unit
+// range, then the cursors), as its launch builds them.
+hipError_t launch_work_queues(const Geom& g, const int* row_ptr, long long col_capacity, int* queue,
+                              hipStream_t s);
 hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpack, const void* vpack,
                               const int* row_ptr, const int* col_idx, long long col_capacity,
                               float scale, void* o, int* queue, int num_cus, hipStream_t s);
