@@ -131,6 +131,30 @@ __device__ inline double wave_max(double x) {
   return x;
 }
 
+// The bitwise threshold searches below fix the threshold's bits from the
+// top.  The threshold they converge to is itself one of the keys (the
+// smallest key kept), so once exactly one key shares the bits fixed so far,
+// that key is the threshold and the remaining rounds can be skipped (checked
+// every fourth round).  Returns true and sets T when that is the case.
+template <int E>
+__device__ inline bool isolated_threshold(const uint64_t (&key)[E], int bit, uint64_t& T) {
+  const uint64_t hi = ~((1ull << bit) - 1ull);
+  int c = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) c += __popcll(__ballot((key[e] & hi) == T));
+  if (c != 1) return false;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot((key[e] & hi) == T);
+    if (b != 0ull) {
+      const int l = __builtin_ctzll(b);
+      const uint32_t lo32 = __shfl((uint32_t)key[e], l), hi32 = __shfl((uint32_t)(key[e] >> 32), l);
+      T = ((uint64_t)hi32 << 32) | lo32;
+    }
+  }
+  return true;
+}
+
 template <int E>
 __global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __restrict__ S, SelectArgs a,
                                                      int* __restrict__ counts, uint32_t* __restrict__ mask,
@@ -174,6 +198,7 @@ __global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __res
 #pragma unroll
       for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(key[e] >= cand));
       if (cnt >= kk) T = cand;
+      if ((bit & 3) == 0 && bit > 0 && isolated_threshold(key, bit, T)) break;
     }
     int gt = 0;
 #pragma unroll
@@ -212,6 +237,7 @@ __global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __res
 #pragma unroll
       for (int e = 0; e < E; ++e) f += (key[e] >= cand) ? p[e] : 0.0;
       if (wave_sum(f) >= target) T = cand;
+      if ((bit & 3) == 0 && bit > 0 && isolated_threshold(key, bit, T)) break;
     }
     double f = 0.0;
 #pragma unroll
