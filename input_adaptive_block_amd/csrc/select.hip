@@ -33,8 +33,8 @@ __global__ __launch_bounds__(256) void scores_kernel(Geom g, const float* __rest
                                                      const float* __restrict__ km, double scale,
                                                      double* __restrict__ S) {
   constexpr int LD = D + 4;
-  __shared__ float qs[kSRows * LD];
-  __shared__ float ks[kSCols * LD];
+  __shared__ __attribute__((aligned(16))) float qs[kSRows * LD];
+  __shared__ __attribute__((aligned(16))) float ks[kSCols * LD];
   const int bh = blockIdx.z;
   if (!head_active(g, bh)) return;  // another scheme's head (whole workgroup)
   const int row0 = blockIdx.x * kSRows, col0 = blockIdx.y * kSCols;
@@ -42,13 +42,20 @@ __global__ __launch_bounds__(256) void scores_kernel(Geom g, const float* __rest
   const int nb = g.nblk;
   const float* qh = qm + (size_t)bh * nb * D;
   const float* kh = km + (size_t)bh * nb * D;
-  for (int t = tid; t < kSRows * D; t += 256) {
-    const int r = t / D, c = t - r * D;
-    qs[r * LD + c] = (row0 + r < nb) ? qh[(size_t)(row0 + r) * D + c] : 0.f;
+  // 16-byte loads and stores (rows of D floats; the LDS row stride D + 4
+  // keeps every row 16-byte aligned)
+  constexpr int V = D / 4;
+  for (int t = tid; t < kSRows * V; t += 256) {
+    const int r = t / V, c = 4 * (t - r * V);
+    const float4 x = (row0 + r < nb) ? *reinterpret_cast<const float4*>(qh + (size_t)(row0 + r) * D + c)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(&qs[r * LD + c]) = x;
   }
-  for (int t = tid; t < kSCols * D; t += 256) {
-    const int r = t / D, c = t - r * D;
-    ks[r * LD + c] = (col0 + r < nb) ? kh[(size_t)(col0 + r) * D + c] : 0.f;
+  for (int t = tid; t < kSCols * V; t += 256) {
+    const int r = t / V, c = 4 * (t - r * V);
+    const float4 x = (col0 + r < nb) ? *reinterpret_cast<const float4*>(kh + (size_t)(col0 + r) * D + c)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(&ks[r * LD + c]) = x;
   }
   __syncthreads();
   const int wr = wave >> 1, wc = wave & 1;
