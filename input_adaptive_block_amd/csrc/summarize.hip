@@ -87,7 +87,9 @@ __device__ inline double sum_identity(int op) {
 __device__ inline float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ inline float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-template <bool BF16, int D, bool PACK, bool SICS>
+// MEAN false: the caller wants no summaries (a SICS-only pass), so the token
+// loop keeps no per-channel reduction at all.
+template <bool BF16, int D, bool PACK, bool SICS, bool MEAN = true>
 __global__ __launch_bounds__(kThreads) void summarize_kernel(
     Geom g, const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     float* __restrict__ q_mean, float* __restrict__ k_mean, uint16_t* __restrict__ qpack,
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
   const int lrow = tid / TPT;    // token slot within a pass
 
   float* mean_out = role == 0 ? q_mean : (role == 1 ? k_mean : nullptr);
-  const bool want_mean = mean_out != nullptr;
+  const bool want_mean = MEAN && mean_out != nullptr;
   float* sics_out = SICS ? (role == 0 ? q_sics : (role == 1 ? k_sics : nullptr)) : nullptr;
   const bool want_sics = SICS && sics_out != nullptr;
 
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) xe[e] = (double)__uint_as_float(x.w[e]);
           }
-          if (l < box.n) {  // padded rows (zeros) take no part in a max or min
+          if (MEAN && l < box.n) {  // padded rows (zeros) take no part in a max or min
 #pragma unroll
             for (int e = 0; e < EPV; ++e) acc[e] = sum_op_t<OP>(acc[e], xe[e]);
           }
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
   for (int off = TPT; off < 64; off <<= 1) {
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-      acc[e] = sum_op(op, acc[e], __shfl_xor(acc[e], off));
+      if (MEAN) acc[e] = sum_op(op, acc[e], __shfl_xor(acc[e], off));
       if (want_sics) uacc[e] += __shfl_xor(uacc[e], off);
     }
   }
@@ -292,12 +294,12 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
   }
 }
 
-template <bool BF16, int D, bool PACK, bool SICS = false>
+template <bool BF16, int D, bool PACK, bool SICS = false, bool MEAN = true>
 hipError_t launch_t(const Geom& g, const void* q, const void* k, const void* v, float* qm, float* km,
                     void* qp, void* kp, void* vp, int roles, hipStream_t s, float* qs = nullptr,
                     float* ks = nullptr) {
   dim3 grid(g.nblk, g.BH, roles);
-  summarize_kernel<BF16, D, PACK, SICS><<<grid, kThreads, 0, s>>>(
+  summarize_kernel<BF16, D, PACK, SICS, MEAN><<<grid, kThreads, 0, s>>>(
       g, q, k, v, qm, km, (uint16_t*)qp, (uint16_t*)kp, (uint16_t*)vp, qs, ks);
   return hipGetLastError();
 }
@@ -307,18 +309,19 @@ hipError_t launch_t(const Geom& g, const void* q, const void* k, const void* v, 
 hipError_t launch_summarize_sics(const Geom& g, bool bf16, const void* q, const void* k, float* q_mean,
                                  float* k_mean, float* q_sics, float* k_sics, hipStream_t s) {
   if (g.BH == 0) return hipSuccess;
+  const bool mean = q_mean != nullptr || k_mean != nullptr;
+#define SPADE_SICS_LAUNCH(B, DD)                                                                          \
+  return mean ? launch_t<B, DD, false, true, true>(g, q, k, nullptr, q_mean, k_mean, nullptr, nullptr,      \
+                                                   nullptr, 2, s, q_sics, k_sics)                          \
+              : launch_t<B, DD, false, true, false>(g, q, k, nullptr, q_mean, k_mean, nullptr, nullptr,     \
+                                                    nullptr, 2, s, q_sics, k_sics)
   if (bf16) {
-    if (g.d == 128)
-      return launch_t<true, 128, false, true>(g, q, k, nullptr, q_mean, k_mean, nullptr, nullptr, nullptr, 2, s,
-                                              q_sics, k_sics);
-    return launch_t<true, 64, false, true>(g, q, k, nullptr, q_mean, k_mean, nullptr, nullptr, nullptr, 2, s,
-                                           q_sics, k_sics);
+    if (g.d == 128) SPADE_SICS_LAUNCH(true, 128);
+    SPADE_SICS_LAUNCH(true, 64);
   }
-  if (g.d == 128)
-    return launch_t<false, 128, false, true>(g, q, k, nullptr, q_mean, k_mean, nullptr, nullptr, nullptr, 2, s,
-                                             q_sics, k_sics);
-  return launch_t<false, 64, false, true>(g, q, k, nullptr, q_mean, k_mean, nullptr, nullptr, nullptr, 2, s,
-                                          q_sics, k_sics);
+  if (g.d == 128) SPADE_SICS_LAUNCH(false, 128);
+  SPADE_SICS_LAUNCH(false, 64);
+#undef SPADE_SICS_LAUNCH
 }
 
 hipError_t launch_summarize(const Geom& g, bool bf16, const void* q, const void* k, const void* v,
