@@ -326,6 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
       for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
     // running max (exp2 domain); finite so that the first rescale factor is 0
     float mref = -1e30f;
+    float mlazy = mref + kLazy;  // a score above this moves the running max
     float lsum = 0.f;
     // asynchronous HBM -> LDS copy of a stage into ring slot `slot`: always
     // two subtiles (the pack buffers carry one spare subtile at their end);
@@ -388,12 +389,13 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
       const float m0 = max3(sx[0], sx[1], sx[2]), m1 = max3(sx[3], sx[4], sx[5]);
       const float m2 = max3(sx[6], sx[7], sx[8]), m3 = max3(sx[9], sx[10], sx[11]);
       const float m4 = max3(sx[12], sx[13], sx[14]);
+      // each lane holds half of its query's keys: a lane whose own maximum
+      // clears the threshold starts the (rare) exchange of the two halves
       float mx = __builtin_elementwise_maximum(max3(m0, m1, m2), max3(m3, m4, sx[15]));
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const float mnew = mx * scale_log2;
-      const bool need = mnew > mref + kLazy;
-      if (__builtin_amdgcn_ballot_w64(need)) {
+      if (__builtin_amdgcn_ballot_w64(mx * scale_log2 > mlazy)) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        const float mnew = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+        const bool need = mnew > mlazy;
         const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
         lsum *= alpha;
 #pragma unroll
@@ -401,6 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[m][v] *= alpha;
         mref = need ? mnew : mref;
+        mlazy = mref + kLazy;
       }
       // first half of the weights (keys of the first 16-key chunk), then the
       // PV MFMAs of that chunk with the second half's exp beside them, then
