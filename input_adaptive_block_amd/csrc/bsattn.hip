@@ -162,8 +162,15 @@ struct Stage {
   int mask;
 };
 
+// The union entry after the last one a stage was taken from, read one block
+// ahead so that no stage waits for its LDS read.
+struct Ahead {
+  uint32_t e;
+  uint32_t n;
+};
+
 __device__ inline Stage next_stage(const Geom& g, const uint32_t* ul, const uint16_t* un, int cnt,
-                                  const Stage& cur) {
+                                  const Stage& cur, Ahead& ah) {
   Stage st = cur;
   if (cur.pos >= 0) {
     const int nsub = (cur.n + 31) >> 5;
@@ -179,10 +186,13 @@ __device__ inline Stage next_stage(const Geom& g, const uint32_t* ul, const uint
     st.pos = -1;
     return st;
   }
-  const int e = __builtin_amdgcn_readfirstlane((int)ul[st.pos]);
+  const int e = __builtin_amdgcn_readfirstlane((int)ah.e);
   st.j = e & 0xFFF;
   st.mask = (int)((unsigned)e >> 12);
-  st.n = __builtin_amdgcn_readfirstlane((int)un[st.pos]);
+  st.n = __builtin_amdgcn_readfirstlane((int)ah.n);
+  const int pa = min(st.pos + 1, cnt - 1);
+  ah.e = ul[pa];
+  ah.n = un[pa];
   st.s0 = 0;
   st.ns = min(2, (st.n + 31) >> 5);
   st.nk = st.n;
@@ -456,10 +466,13 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     // while stages s+1 and s+2 are in flight; one barrier per stage ----
     Stage none;
     none.pos = -1; none.j = 0; none.n = 0; none.s0 = 0; none.ns = 0; none.nk = 0; none.mask = 0;
-    Stage cur = next_stage(g, ulist, ublkn, ucnt, none);
+    Ahead ahead;
+    ahead.e = ulist[0];
+    ahead.n = ublkn[0];
+    Stage cur = next_stage(g, ulist, ublkn, ucnt, none, ahead);
     if (cur.pos >= 0) {
-      Stage nxt = next_stage(g, ulist, ublkn, ucnt, cur);
-      Stage nn = nxt.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, nxt) : none;
+      Stage nxt = next_stage(g, ulist, ublkn, ucnt, cur, ahead);
+      Stage nn = nxt.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, nxt, ahead) : none;
       issue(cur, 0);
       if (nxt.pos >= 0) issue(nxt, 1);
       if (nn.pos >= 0) issue(nn, 2);
@@ -490,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
         }
         // stage s+3 goes into the slot of stage s-1, which every wave left
         // before the barrier above
-        const Stage n3 = nn.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, nn) : none;
+        const Stage n3 = nn.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, nn, ahead) : none;
         if (n3.pos >= 0) issue(n3, (slot + 3) & 3);
         cur = nxt;
         nxt = nn;
