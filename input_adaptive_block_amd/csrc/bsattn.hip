@@ -149,54 +149,46 @@ __global__ __launch_bounds__(kQThreads) void queue_kernel(Geom g, int U, const i
 // bf16 attention
 // ---------------------------------------------------------------------------
 
-// Position in the unit's union list: block j (entry pos), subtiles
-// [s0, s0 + ns) of it, nk valid keys from subtile s0 on, mask of the unit's
-// rows that keep the block.
-struct Stage {
-  int pos;  // -1: no stage
-  int j;
-  int n;
+// A walk over the unit's union list, one stage (two 32-key subtiles of one
+// block) at a time: entry pos, its first subtile s0, the block's token count n
+// and the entry word (block id | mask of the unit's rows keeping it << 12).
+// The entry after pos is read one block ahead (ae, an), so that a new block
+// never waits for its LDS read.
+struct Cursor {
+  int pos;
   int s0;
-  int ns;
-  int nk;
-  int mask;
+  int n;
+  int word;
+  uint32_t ae;
+  uint32_t an;
 };
 
-// The union entry after the last one a stage was taken from, read one block
-// ahead so that no stage waits for its LDS read.
-struct Ahead {
-  uint32_t e;
-  uint32_t n;
-};
+__device__ inline void cursor_take(Cursor& c, const uint32_t* ul, const uint16_t* un, int cnt) {
+  c.word = __builtin_amdgcn_readfirstlane((int)c.ae);
+  c.n = __builtin_amdgcn_readfirstlane((int)c.an);
+  const int pa = min(c.pos + 1, cnt - 1);
+  c.ae = ul[pa];
+  c.an = un[pa];
+}
 
-__device__ inline Stage next_stage(const Geom& g, const uint32_t* ul, const uint16_t* un, int cnt,
-                                  const Stage& cur, Ahead& ah) {
-  Stage st = cur;
-  if (cur.pos >= 0) {
-    const int nsub = (cur.n + 31) >> 5;
-    st.s0 = cur.s0 + cur.ns;
-    if (st.s0 < nsub) {
-      st.ns = min(2, nsub - st.s0);
-      st.nk = cur.n - 32 * st.s0;
-      return st;
-    }
+__device__ inline Cursor cursor_start(const uint32_t* ul, const uint16_t* un, int cnt) {
+  Cursor c;
+  c.pos = 0;
+  c.s0 = 0;
+  c.n = 0;
+  c.word = 0;
+  c.ae = ul[0];
+  c.an = un[0];
+  if (cnt > 0) cursor_take(c, ul, un, cnt);
+  return c;
+}
+
+__device__ inline void cursor_next(Cursor& c, const uint32_t* ul, const uint16_t* un, int cnt) {
+  c.s0 += 2;
+  if (32 * c.s0 >= c.n) {
+    c.s0 = 0;
+    if (++c.pos < cnt) cursor_take(c, ul, un, cnt);
   }
-  st.pos = cur.pos + 1;
-  if (st.pos >= cnt) {
-    st.pos = -1;
-    return st;
-  }
-  const int e = __builtin_amdgcn_readfirstlane((int)ah.e);
-  st.j = e & 0xFFF;
-  st.mask = (int)((unsigned)e >> 12);
-  st.n = __builtin_amdgcn_readfirstlane((int)ah.n);
-  const int pa = min(st.pos + 1, cnt - 1);
-  ah.e = ul[pa];
-  ah.n = un[pa];
-  st.s0 = 0;
-  st.ns = min(2, (st.n + 31) >> 5);
-  st.nk = st.n;
-  return st;
 }
 
 // s_waitcnt immediate on gfx9: vmcnt in bits 3:0
@@ -343,11 +335,10 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     // wave w copies KB w*CPW .. w*CPW+CPW-1 of K and of V, lane L's 16 bytes
     // land at 16 L.  M0 holds the wave's LDS destination.
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)ring;
-    auto issue = [&](const Stage& st, int slot) __attribute__((always_inline)) {
-      const size_t src = head_off + (size_t)st.j * g.P * D + (size_t)st.s0 * SUB;
+    auto issue = [&](const Cursor& st, int slot) __attribute__((always_inline)) {
+      const size_t src = head_off + (size_t)(st.word & 0xFFF) * g.P * D + (size_t)st.s0 * SUB;
       const char* ks = reinterpret_cast<const char*>(kpack + src) + lane * 16;
       const char* vs = reinterpret_cast<const char*>(vpack + src) + lane * 16;
-      if (wave >= kCopyWaves) return;
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
         const int t = wave * CPW + c;
@@ -464,53 +455,62 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
 
     // ---- stage ring of four slots: stage s is computed from slot s % 4
     // while stages s+1 and s+2 are in flight; one barrier per stage ----
-    Stage none;
-    none.pos = -1; none.j = 0; none.n = 0; none.s0 = 0; none.ns = 0; none.nk = 0; none.mask = 0;
-    Ahead ahead;
-    ahead.e = ulist[0];
-    ahead.n = ublkn[0];
-    Stage cur = next_stage(g, ulist, ublkn, ucnt, none, ahead);
-    if (cur.pos >= 0) {
-      Stage nxt = next_stage(g, ulist, ublkn, ucnt, cur, ahead);
-      Stage nn = nxt.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, nxt, ahead) : none;
-      issue(cur, 0);
-      if (nxt.pos >= 0) issue(nxt, 1);
-      if (nn.pos >= 0) issue(nn, 2);
-      bool did_prev = true;  // no LDS reads of this unit are outstanding yet
-      int slot = 0;
-      for (;;) {
-        // own copies of this stage have landed (those of the next two may
-        // still fly); a wave that skipped the previous stage may still have
-        // reads of the slot about to be refilled outstanding
-        if (nn.pos >= 0) {
+    // Every wave walks the stages it computes (cc); the copying waves also
+    // walk the stages they copy (kc), three ahead.  Stage s lives in ring
+    // slot s % 4.
+    const bool copier = wave < kCopyWaves;
+    Cursor cc = cursor_start(ulist, ublkn, ucnt);
+    Cursor kc = cc;
+    int si = 0;      // stage computed next
+    int issued = 0;  // stages this copying wave has issued
+    if (copier) {
+      for (int p = 0; p < 3 && kc.pos < ucnt; ++p) {
+        issue(kc, issued & 3);
+        ++issued;
+        cursor_next(kc, ulist, ublkn, ucnt);
+      }
+    }
+    bool did_prev = true;  // no LDS reads of this unit are outstanding yet
+    while (cc.pos < ucnt) {
+      // own copies of this stage have landed (those of the next two may still
+      // fly); a wave that skipped the previous stage may still have reads of
+      // the slot about to be refilled outstanding
+      if (copier) {
+        const int fly = issued - si - 1;
+        if (__builtin_expect(fly >= 2 && did_prev, 1)) {
+          __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * PER));
+        } else if (fly >= 2) {
           if (did_prev) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * PER));
           else __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * PER) & ~(15 << 8));
-        } else if (nxt.pos >= 0) {
+        } else if (fly == 1) {
           if (did_prev) __builtin_amdgcn_s_waitcnt(vm_wait_imm(PER));
           else __builtin_amdgcn_s_waitcnt(vm_wait_imm(PER) & ~(15 << 8));
         } else {
           if (did_prev) __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
           else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0) & ~(15 << 8));
         }
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        did_prev = active && ((cur.mask >> my_row) & 1);
-        if (did_prev) {
-          const int kb = slot * 4 * SUB;
-#pragma unroll 1
-          for (int t = 0; t < cur.ns; ++t) step(min(32, cur.nk - 32 * t), kb + t * SUB, kb + 2 * SUB + t * SUB);
-        }
-        // stage s+3 goes into the slot of stage s-1, which every wave left
-        // before the barrier above
-        const Stage n3 = nn.pos >= 0 ? next_stage(g, ulist, ublkn, ucnt, nn, ahead) : none;
-        if (n3.pos >= 0) issue(n3, (slot + 3) & 3);
-        cur = nxt;
-        nxt = nn;
-        nn = n3;
-        slot = (slot + 1) & 3;
-        if (cur.pos < 0) break;
+      } else if (!did_prev) {
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0) & ~(15 << 8));
       }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      did_prev = active && ((cc.word >> (12 + my_row)) & 1);
+      if (did_prev) {
+        const int kb = (si & 3) * 4 * SUB;
+        const int nk = cc.n - 32 * cc.s0;
+        step(min(32, nk), kb, kb + 2 * SUB);
+        if (nk > 32) step(min(32, nk - 32), kb + SUB, kb + 3 * SUB);
+      }
+      // stage s+3 goes into the slot of stage s-1, which every wave left
+      // before the barrier above
+      if (copier && kc.pos < ucnt) {
+        issue(kc, issued & 3);
+        ++issued;
+        cursor_next(kc, ulist, ublkn, ucnt);
+      }
+      cursor_next(cc, ulist, ublkn, ucnt);
+      ++si;
     }
 
     if (active) {
