@@ -49,6 +49,7 @@
 //   rounded values, so normalisation matches the weights PV used.  The PV
 //   MFMAs of the first 16 keys of a lane run while the exp of its second 16
 //   is computed.
+#include <type_traits>
 #include "spade_internal.h"
 
 namespace spade {
@@ -356,7 +357,13 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     // lazy rescale, p = exp2(S scale - m) rounded to bf16 and its row sum,
     // then O^T += V^T P^T (8 MFMAs; V operands read two MFMAs ahead).  Three
     // wavefronts per SIMD overlap one wave's softmax with the others' MFMAs.
-    auto step = [&](int kvalid, int kx, int vx) __attribute__((always_inline)) {
+    //
+    // VE (a compile-time constant) is the number of each lane's 16 scores that
+    // are real keys when that does not depend on the lane (12 for 24 valid
+    // keys); VE = 0 masks the keys from kvalid when it is below 32.
+    auto step = [&](auto ve_c, int kvalid, int kx, int vx) __attribute__((always_inline)) {
+      constexpr int VE = decltype(ve_c)::value;
+      constexpr int NP = VE == 0 ? 8 : VE / 2;  // pairs of scores that can hold a real key
       const bf16x8* kl = reinterpret_cast<const bf16x8*>(ring + kx);
       const bf16x8* vl = reinterpret_cast<const bf16x8*>(ring + vx);
       bf16x8 kr[3];
@@ -377,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
       bf16x8 vr[3];
       vr[0] = vl[(2 * (0 % NM) + 0 / NM) * 64 + lane];
       vr[1] = vl[(2 * (1 % NM) + 1 / NM) * 64 + lane];
-      if (kvalid < 32) {
+      if (VE == 0 && kvalid < 32) {
         const int kk = kvalid - 4 * half;  // key of element v: 8 (v/4) + 4 half + v%4
 #pragma unroll
         for (int v = 0; v < 16; ++v)
@@ -389,10 +396,15 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
       };
       const float m0 = max3(sx[0], sx[1], sx[2]), m1 = max3(sx[3], sx[4], sx[5]);
       const float m2 = max3(sx[6], sx[7], sx[8]), m3 = max3(sx[9], sx[10], sx[11]);
-      const float m4 = max3(sx[12], sx[13], sx[14]);
+      float mx;
+      if constexpr (VE == 12) {
+        mx = __builtin_elementwise_maximum(max3(m0, m1, m2), m3);
+      } else {
+        const float m4 = max3(sx[12], sx[13], sx[14]);
+        mx = __builtin_elementwise_maximum(max3(m0, m1, m2), max3(m3, m4, sx[15]));
+      }
       // each lane holds half of its query's keys: a lane whose own maximum
       // clears the threshold starts the (rare) exchange of the two halves
-      float mx = __builtin_elementwise_maximum(max3(m0, m1, m2), max3(m3, m4, sx[15]));
       if (__builtin_amdgcn_ballot_w64(mx * scale_log2 > mlazy)) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         const float mnew = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
@@ -429,10 +441,15 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int e = 4 + i * 4 / NM; e < 4 + (i + 1) * 4 / NM; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[2 * e], scale_log2, -mref));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[2 * e + 1], scale_log2, -mref));
-          pr[e][0] = (__bf16)p0;
-          pr[e][1] = (__bf16)p1;
+          if (e < NP) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[2 * e], scale_log2, -mref));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[2 * e + 1], scale_log2, -mref));
+            pr[e][0] = (__bf16)p0;
+            pr[e][1] = (__bf16)p1;
+          } else {
+            pr[e][0] = (__bf16)0.f;  // padding keys weigh nothing
+            pr[e][1] = (__bf16)0.f;
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -447,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int e = (i - NM) * 8 / NM; e < (i - NM + 1) * 8 / NM; ++e)
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
+          if (e < NP) lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
@@ -498,9 +515,24 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
       did_prev = active && ((cc.word >> (12 + my_row)) & 1);
       if (did_prev) {
         const int kb = (si & 3) * 4 * SUB;
+        using k24_t = std::integral_constant<int, 12>;
+        using any_t = std::integral_constant<int, 0>;
+        // the stage's first subtile, then its second through the same code,
+        // unless the second holds 24 keys (the last subtile of a 120-token
+        // block), which has a step of its own
         const int nk = cc.n - 32 * cc.s0;
-        step(min(32, nk), kb, kb + 2 * SUB);
-        if (nk > 32) step(min(32, nk - 32), kb + SUB, kb + 3 * SUB);
+        int kx = kb, kv = min(32, nk), rest = nk - 32;
+        for (;;) {
+          step(any_t{}, kv, kx, kx + 2 * SUB);
+          if (rest <= 0) break;
+          if (rest == 24) {
+            step(k24_t{}, 24, kb + SUB, kb + 3 * SUB);
+            break;
+          }
+          kx = kb + SUB;
+          kv = min(32, rest);
+          rest = 0;
+        }
       }
       // stage s+3 goes into the slot of stage s-1, which every wave left
       // before the barrier above
