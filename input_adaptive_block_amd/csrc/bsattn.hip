@@ -24,9 +24,11 @@
 //   the others' MFMAs.
 // * Scores are computed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_bf16: each lane owns one query and 16 keys, so the row
-//   max and row sum are in-lane plus one permlane32 swap, and the S^T
-//   accumulator converted to bf16 is directly the B operand of
-//   O^T += V^T P^T.  Q operands stay in registers for the unit.
+//   sum is in-lane plus one permlane32 swap at the end, the lazy-rescale test
+//   runs on each lane's own maximum (the two halves of a query exchange maxima
+//   only when a lane clears it), and the S^T accumulator converted to bf16 is
+//   directly the B operand of O^T += V^T P^T.  Q operands stay in registers
+//   for the unit.
 // * K and V come pre-packed (by the summarize kernel) in MFMA operand order:
 //   a stage (two 32-key subtiles of K and of V, 32 KB at d = 128) is a
 //   contiguous HBM -> LDS copy issued with global_load_lds_dwordx4 by eight
@@ -36,9 +38,15 @@
 //   s+3 are in flight.  Each copying wave issues stage s+3 into the slot of
 //   stage s-1 right after its own steps of stage s (every wave left that
 //   slot before the barrier of stage s), so the copies are issued while the
-//   other waves still compute.  Operands are read just ahead of their MFMAs
-//   into small register rings, which keeps a wavefront within the 168
-//   registers that three wavefronts per SIMD allow.
+//   other waves still compute.  Every wave walks the stages it computes with
+//   a small cursor; only the copying waves also walk the stages they copy.
+//   The youngest wave of a SIMD loses the MFMA arbitration and ends each stage
+//   last, so the instructions between its steps are kept few.  Operands are
+//   read just ahead of their MFMAs into small register rings, which keeps a
+//   wavefront within the 168 registers that three wavefronts per SIMD allow.
+//   The step is compiled twice: for any subtile (a per-key mask when fewer
+//   than 32 keys are real), and for one with 24 real keys (the last subtile
+//   of a 120-token block), which skips the mask and the padding's exps.
 // * A wavefront raises its issue priority for its runs of MFMAs, so a wave
 //   that reaches its MFMAs keeps the matrix pipe while the others run their
 //   softmax arithmetic beside it.
