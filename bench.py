@@ -59,10 +59,16 @@ def kept_flops(cfg, rp, ci):
 
 
 def source_hash():
+    """Hash of the attention kernel's code: its sources with // comments,
+    trailing blanks and empty lines removed, so that a comment edit keeps the
+    counters that were taken on the same code."""
     h = hashlib.sha256()
     for f in ("bsattn.hip", "spade_internal.h"):
-        with open(os.path.join(ROOT, "input_adaptive_block_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "input_adaptive_block_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
