@@ -158,6 +158,11 @@ TEST_CONFIGS = {
     "max_block_tokens": Config("max_block_tokens", B=1, H=1, d=128, T=8, Hh=32, W=32, bt=4, bh=16, bw=16,
                                dtype="bf16", sigma=0.5, amp_kind="const", amp_params=(1.0,),
                                mode=MODE_COUNT, budget=(3,), seed=22),
+    # 56-token blocks (a full 32-key subtile, then 24 keys) with 24-token
+    # partial blocks along w (17 = 7 + 7 + 3).
+    "tail24": Config("tail24", B=1, H=2, d=128, T=4, Hh=8, W=17, bt=2, bh=4, bw=7,
+                     dtype="bf16", sigma=0.5, amp_kind="uniform", amp_params=(0.3, 2.0),
+                     mode=MODE_MASS, budget=(0.7,), seed=23),
     # fp32 (debug) path on a ragged shape.
     "ragged_f32": Config("ragged_f32", B=1, H=2, d=128, T=5, Hh=7, W=9, bt=4, bh=4, bw=4,
                          dtype="f32", sigma=1.0, amp_kind="const", amp_params=(0.0,),

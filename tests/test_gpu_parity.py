@@ -30,7 +30,7 @@ import input_adaptive_block_amd as spade  # noqa: E402
 BF16_TOL = 2e-2
 F32_TOL = 1e-5
 SMALL = ["tiny", "tiny_bf16", "ragged_p64", "mid_shape", "small_shape", "ragged_small", "big_block",
-         "token_level", "one_block", "d64", "ragged_f32"]
+         "token_level", "one_block", "d64", "tail24", "ragged_f32"]
 
 
 # ---------------------------------------------------------------------------
