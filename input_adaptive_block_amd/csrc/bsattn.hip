@@ -479,10 +479,10 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     };
 
     // ---- stage ring of four slots: stage s is computed from slot s % 4
-    // while stages s+1 and s+2 are in flight; one barrier per stage ----
+    // while stages s+1 and s+2 are in flight, and stage s+3 is issued at its
+    // end; one barrier per stage ----
     // Every wave walks the stages it computes (cc); the copying waves also
-    // walk the stages they copy (kc), three ahead.  Stage s lives in ring
-    // slot s % 4.
+    // walk the stages they copy (kc), three ahead.
     const bool copier = wave < kCopyWaves;
     Cursor cc = cursor_start(ulist, ublkn, ucnt);
     Cursor kc = cc;
