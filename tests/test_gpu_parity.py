@@ -300,6 +300,32 @@ def test_attention_matches_oracle(name):
     assert compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), name) == 0
 
 
+# a different budget for every head: each head's rows are selected with its
+# own k, ratio or mass
+PER_HEAD = [("mid_shape", "mass", [0.5, 0.97]), ("small_shape", "ratio", [0.1, 0.6]),
+            ("ragged_small", "count", [2, 9]), ("d64", "mass", [0.95, 0.3])]
+
+
+@pytest.mark.parametrize("name,mode,budget", PER_HEAD)
+def test_per_head_budgets_match_oracle(name, mode, budget):
+    cfg = synth.get_config(name)
+    assert cfg.H == len(budget)
+    x = synth.make_inputs(cfg)
+    g = geom(cfg)
+    o, rp, ci = run_attn(cfg, x, mode=mode, budget=budget)
+    rp, ci = csr_rows(rp, ci)
+    scale = oracle.default_scale(cfg.d)
+    S_ref = oracle.estimate(oracle_means(cfg, x["q"]), oracle_means(cfg, x["k"]), scale)
+    sel = oracle.select(S_ref, mode, budget)
+    assert compare_selection(sel, rp, ci, S_ref, mode, budget, name) == 0
+    kept = np.diff(rp).reshape(cfg.B, cfg.H, g.nblk).sum(axis=(0, 2))
+    assert kept[0] != kept[1]  # the heads really keep different amounts
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], g, rp, ci, scale)
+    err = np.abs(dev_to_f64(o) - ref).max()
+    assert err <= BF16_TOL, err
+
+
 # the supported limits: 4096 and 1728 blocks per head (the widest selection
 # rows), and 1024-token blocks (eight 128-query tiles per row, 32 key subtiles
 # per block)
