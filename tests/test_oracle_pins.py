@@ -282,20 +282,82 @@ def test_keep_count_ratio_rounding():
 
 
 def test_margin_bounds_flip_distance():
-    """Perturbing S by less than margin/2 never changes the kept set."""
+    """Perturbing S by less than a fraction of the margin never changes the
+    kept set.  Top-k: every score moves by < margin / 2, so the k-th and
+    (k+1)-th stay apart.  Mass: with every score moved by at most eps, the
+    mass of any fixed subset changes by a factor within exp(+-2 eps), so the
+    mass of the best (k-1)- and k-subsets moves by at most exp(2 eps) - 1; for
+    eps = 0.1 m that is < 0.23 m, below both mass terms of the margin, and
+    2 eps < the score gap, so the prefix length and the kept set stay."""
     S = _random_rows(60, 12, seed=9)
     rng = np.random.default_rng(1)
+    checked = {"count": 0, "mass": 0}
     for mode, val in (("count", 4), ("mass", 0.8)):
         sel = oracle.select(S[None, None], mode, [val])
         for r in range(S.shape[0]):
             m = sel.margins[r]
             if not np.isfinite(m) or m <= 1e-9:
                 continue
-            eps = 0.45 * m if mode == "count" else 0.2 * m
-            pert = S[r] + rng.uniform(-eps, eps, size=S.shape[1]) * (0.5 if mode == "mass" else 1.0)
-            sel2 = oracle.select(pert[None, None, None], mode, [val])
-            if mode == "count":
-                assert sel2.row(0).tolist() == sel.row(r).tolist()
+            eps = 0.45 * m if mode == "count" else 0.1 * m
+            for _ in range(4):
+                pert = S[r] + rng.uniform(-eps, eps, size=S.shape[1])
+                sel2 = oracle.select(pert[None, None, None], mode, [val])
+                assert sel2.row(0).tolist() == sel.row(r).tolist(), (mode, r, m)
+            checked[mode] += 1
+    assert checked["count"] > 20 and checked["mass"] > 20
+
+
+# Hand-worked mass rows (softmax weights in closed form): with
+# S = [ln 4, ln 2, 0, 0] the weights are [4, 2, 1, 1] / 8, so the cumulative
+# masses in score order are C = [1/2, 3/4, 7/8, 1].
+#  * tau = 0.6 keeps 2 blocks (C_1 = 0.5 < 0.6 <= C_2 = 0.75); the three terms
+#    are S_(2) - S_(3) = ln 2, C_2 - tau = 0.15, tau - C_1 = 0.1: margin 0.1.
+#  * tau = 0.72 keeps 2 blocks; terms ln 2, 0.03, 0.22: margin 0.03.
+#  * S = [ln 4, ln 2 + 0.01, ln 2, 0] with tau = 0.5: Z = 7 + 2 e^0.01, C_1 =
+#    4 / Z < 0.5 <= C_2, terms 0.01, C_2 - 0.5 = 0.167..., 0.5 - 4/Z = 0.0565...:
+#    margin 0.01 (the score gap).
+MASS_ROWS = [
+    ([math.log(4), math.log(2), 0.0, 0.0], 0.6, 2, lambda t: t - 0.5),
+    ([math.log(4), math.log(2), 0.0, 0.0], 0.72, 2, lambda t: 0.75 - t),
+    ([math.log(4), math.log(2) + 0.01, math.log(2), 0.0], 0.5, 2, lambda t: 0.01),
+]
+
+
+@pytest.mark.parametrize("row,tau,k,margin", MASS_ROWS)
+def test_mass_margin_hand_worked(row, tau, k, margin):
+    """Each of the three mass-margin terms is the binding one on one row (tau
+    is taken as its fp32 value, the boundary's budget type)."""
+    S = np.array(row)[None, None, None]
+    sel = oracle.select(S, "mass", [tau])
+    assert sel.counts[0] == k
+    assert abs(sel.margins[0] - margin(float(np.float32(tau)))) < 1e-12
+
+
+def _mass_margin_variant(row, tau, drop=None, unnormalised=False):
+    """The mass margin restated with one planted mistake: a dropped term
+    ("gap", "above", "below") or the cumulative mass compared unnormalised."""
+    s = np.sort(np.asarray(row, dtype=np.float64))[::-1]
+    p = np.exp(s - s[0])
+    Z = p.sum()
+    c = np.cumsum(p) if unnormalised else np.cumsum(p) / Z
+    k = int(np.nonzero(c >= tau)[0][0]) + 1 if (c >= tau).any() else len(s)
+    terms = {"gap": s[k - 1] - s[k] if k < len(s) else math.inf,
+             "above": c[k - 1] - tau,
+             "below": tau - (c[k - 2] if k >= 2 else 0.0)}
+    if drop is not None:
+        del terms[drop]
+    return min(terms.values())
+
+
+@pytest.mark.parametrize("drop,unnormalised", [("gap", False), ("above", False), ("below", False), (None, True)])
+def test_planted_mass_margin_mistakes_are_caught(drop, unnormalised):
+    """Dropping any one term of the mass margin, or comparing unnormalised
+    cumulative mass against tau, gives a wrong value on one of the
+    hand-worked rows."""
+    for row, tau, _, m in MASS_ROWS:  # the restatement itself is right
+        assert abs(_mass_margin_variant(row, tau) - m(tau)) < 1e-12
+    wrong = [abs(_mass_margin_variant(row, tau, drop, unnormalised) - m(tau)) > 1e-6 for row, tau, _, m in MASS_ROWS]
+    assert any(wrong)
 
 
 def test_shift_of_all_keys_leaves_selection_and_attention():
