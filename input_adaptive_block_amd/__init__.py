@@ -14,7 +14,7 @@ from ._lib import (  # noqa: F401
     SPADE_SUM_MAX, SPADE_SUM_MEAN, SPADE_SUM_MIN,
     SPADE_KEEP_COUNT, SPADE_KEEP_MASS, SPADE_KEEP_RATIO, SPADE_OK, SPADE_ERR_CAPACITY,
     SPADE_ERR_DEVICE, SPADE_ERR_INVALID_ARG, SPADE_ERR_UNSUPPORTED, lib, spade_attn,
-    spade_block_sparse_attn, spade_check, spade_debug_scores, spade_debug_work_queues, spade_estimate_select,
+    spade_block_sparse_attn, spade_check, spade_debug_scores, spade_estimate_select,
     spade_attn_schemes, spade_max_nnz, spade_num_blocks, spade_profile_events, spade_scheme_select,
     spade_schemes_workspace_bytes, spade_summarize, spade_summarize_sics,
     spade_workspace_bytes,
@@ -26,7 +26,7 @@ __all__ = [
     "block_sparse_attn", "attn", "debug_scores", "alloc_workspace", "scheme_select", "attn_schemes",
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
     "spade_summarize", "spade_summarize_sics", "spade_estimate_select", "spade_block_sparse_attn", "spade_attn",
-    "spade_debug_scores", "spade_debug_work_queues", "spade_schemes_workspace_bytes", "spade_scheme_select", "spade_attn_schemes",
+    "spade_debug_scores", "spade_schemes_workspace_bytes", "spade_scheme_select", "spade_attn_schemes",
 ]
 
 
@@ -55,16 +55,55 @@ def problem_for(q, grid: Sequence[int], block: Sequence[int], scale: Optional[fl
                    SUMMARIZERS[summarizer])
 
 
-def _check_tensor(t, name, shape=None, dtype=None):
+def _check_tensor(t, name, shape=None, dtype=None, device=None):
+    _check_tensors([(t, name, shape, dtype)], device)
+
+
+def _check_tensors(specs, device=None):
+    """Raise SpadeError unless every (tensor, name, shape, dtype) of specs is
+    a contiguous tensor of that shape and dtype (None: any) and all of them are
+    device tensors on `device` (None: the first one's).  Forms are checked for
+    every tensor before any device, so each check can be exercised without a
+    GPU."""
     torch = _torch()
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-    if dtype is not None and t.dtype != dtype:
-        raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} has dtype {t.dtype}, expected {dtype}")
+    for t, name, shape, dtype in specs:
+        if not isinstance(t, torch.Tensor):
+            raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} must be a tensor")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if dtype is not None and t.dtype != dtype:
+            raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} must be contiguous")
+    for t, name, _, _ in specs:
+        if not t.is_cuda:
+            raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} must be a device tensor")
+        if device is None:
+            device = t.device
+        if t.device != device:
+            raise SpadeError(SPADE_ERR_INVALID_ARG, f"{name} is on {t.device}, expected {device}")
+
+
+def _workspace_specs(ws, problem: Problem):
+    """[] for no caller workspace, else the workspace's spec for
+    _check_tensors (a one-dimensional uint8 tensor); a uint8 workspace below
+    spade_workspace_bytes raises SPADE_ERR_CAPACITY."""
+    torch = _torch()
+    if ws is None:
+        return []
+    if isinstance(ws, torch.Tensor) and ws.dtype == torch.uint8:
+        need = spade_workspace_bytes(problem)
+        if ws.numel() < need:
+            raise SpadeError(SPADE_ERR_CAPACITY, f"workspace has {ws.numel()} bytes, needs {need}")
+        return [(ws, "workspace", (ws.numel(),), torch.uint8)]
+    return [(ws, "workspace", None, torch.uint8)]
+
+
+def _summary_shape(problem: Problem):
+    nblk = spade_num_blocks(problem)
+    if nblk < 0:
+        raise SpadeError(spade_check(problem), "problem")
+    return (problem.B, problem.H, nblk, problem.d)
 
 
 def alloc_workspace(problem: Problem, device=None):
@@ -81,8 +120,7 @@ def summarize(q, k, grid, block, summarizer: str = "mean") -> Tuple["object", "o
     nblk = spade_num_blocks(p)
     if nblk < 0:
         raise SpadeError(spade_check(p), "summarize")
-    _check_tensor(q, "q")
-    _check_tensor(k, "k", q.shape, q.dtype)
+    _check_tensors([(q, "q", None, None), (k, "k", q.shape, q.dtype)])
     qm = torch.empty(p.B, p.H, nblk, p.d, dtype=torch.float32, device=q.device)
     km = torch.empty_like(qm)
     spade_summarize(p, q, k, qm, km)
@@ -97,8 +135,7 @@ def summarize_sics(q, k, grid, block, summarizer: str = "mean"):
     nblk = spade_num_blocks(p)
     if nblk < 0:
         raise SpadeError(spade_check(p), "summarize_sics")
-    _check_tensor(q, "q")
-    _check_tensor(k, "k", q.shape, q.dtype)
+    _check_tensors([(q, "q", None, None), (k, "k", q.shape, q.dtype)])
     qm = torch.empty(p.B, p.H, nblk, p.d, dtype=torch.float32, device=q.device)
     km = torch.empty_like(qm)
     qs = torch.empty(p.B, p.H, nblk, dtype=torch.float32, device=q.device)
@@ -110,15 +147,18 @@ def summarize_sics(q, k, grid, block, summarizer: str = "mean"):
 def estimate_select(q_mean, k_mean, problem: Problem, mode, per_head: Sequence[float], workspace=None,
                     window=None):
     torch = _torch()
+    shape = _summary_shape(problem)
+    _check_tensors([(q_mean, "q_mean", shape, torch.float32), (k_mean, "k_mean", shape, torch.float32)]
+                   + _workspace_specs(workspace, problem))
     bud = Budget(mode, per_head, window)
     cap = spade_max_nnz(problem, bud)
     if cap < 0:
         raise SpadeError(spade_check(problem, bud), "estimate_select")
     nblk = spade_num_blocks(problem)
     R = problem.B * problem.H * nblk
+    ws = alloc_workspace(problem, q_mean.device) if workspace is None else workspace
     row_ptr = torch.empty(R + 1, dtype=torch.int32, device=q_mean.device)
     col_idx = torch.empty(max(1, cap), dtype=torch.int32, device=q_mean.device)
-    ws = alloc_workspace(problem, q_mean.device) if workspace is None else workspace
     spade_estimate_select(problem, q_mean, k_mean, bud, row_ptr, col_idx, cap, ws, ws.numel())
     return row_ptr, col_idx
 
@@ -126,11 +166,16 @@ def estimate_select(q_mean, k_mean, problem: Problem, mode, per_head: Sequence[f
 def block_sparse_attn(q, k, v, grid, block, row_ptr, col_idx, scale=None, workspace=None, out=None):
     torch = _torch()
     p = problem_for(q, grid, block, scale)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(t, name, q.shape, q.dtype)
-    _check_tensor(row_ptr, "row_ptr", dtype=torch.int32)
-    _check_tensor(col_idx, "col_idx", dtype=torch.int32)
+    nblk = _summary_shape(p)[2]
     o = torch.empty_like(q) if out is None else out
+    # the kernels read row_ptr[0 .. R]; col_idx is read only below the
+    # capacity passed with it (its length)
+    if not isinstance(col_idx, torch.Tensor) or col_idx.dim() != 1:
+        raise SpadeError(SPADE_ERR_INVALID_ARG, "col_idx must be a one-dimensional tensor")
+    _check_tensors([(q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype), (v, "v", q.shape, q.dtype),
+                    (row_ptr, "row_ptr", (p.B * p.H * nblk + 1,), torch.int32),
+                    (col_idx, "col_idx", None, torch.int32), (o, "out", q.shape, q.dtype)]
+                   + _workspace_specs(workspace, p))
     ws = alloc_workspace(p, q.device) if workspace is None else workspace
     spade_block_sparse_attn(p, q, k, v, row_ptr, col_idx, col_idx.numel(), o, ws, ws.numel())
     return o
@@ -142,25 +187,27 @@ def attn(q, k, v, grid, block, mode, per_head: Sequence[float], scale=None, work
     window's radii (rt, rh, rw) in blocks, united with the scored blocks."""
     torch = _torch()
     p = problem_for(q, grid, block, scale, summarizer)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(t, name, q.shape, q.dtype)
+    _check_tensors([(q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype), (v, "v", q.shape, q.dtype)]
+                   + _workspace_specs(workspace, p))
     bud = Budget(mode, per_head, window)
     cap = spade_max_nnz(p, bud)
     if cap < 0:
         raise SpadeError(spade_check(p, bud), "attn")
     nblk = spade_num_blocks(p)
     R = p.B * p.H * nblk
+    ws = alloc_workspace(p, q.device) if workspace is None else workspace
     row_ptr = torch.empty(R + 1, dtype=torch.int32, device=q.device)
     col_idx = torch.empty(max(1, cap), dtype=torch.int32, device=q.device)
     o = torch.empty_like(q)
-    ws = alloc_workspace(p, q.device) if workspace is None else workspace
     spade_attn(p, q, k, v, bud, o, row_ptr, col_idx, cap, ws, ws.numel())
     return o, row_ptr, col_idx
 
 
 def debug_scores(q_mean, k_mean, problem: Problem):
     torch = _torch()
-    nblk = spade_num_blocks(problem)
+    shape = _summary_shape(problem)
+    _check_tensors([(q_mean, "q_mean", shape, torch.float32), (k_mean, "k_mean", shape, torch.float32)])
+    nblk = shape[2]
     S = torch.empty(problem.B, problem.H, nblk, nblk, dtype=torch.float64, device=q_mean.device)
     spade_debug_scores(problem, q_mean, k_mean, S)
     return S
@@ -171,8 +218,7 @@ def scheme_select(q, k, grid, candidates, summarizer: str = "mean"):
     choice: returns (agg [C, B, H] fp32, scheme [B, H] int32)."""
     torch = _torch()
     p = problem_for(q, grid, candidates[0], summarizer=summarizer)
-    _check_tensor(q, "q")
-    _check_tensor(k, "k", q.shape, q.dtype)
+    _check_tensors([(q, "q", None, None), (k, "k", q.shape, q.dtype)])
     n = spade_schemes_workspace_bytes(p, candidates)
     if n == 0:
         raise SpadeError(SPADE_ERR_INVALID_ARG, "scheme_select")
@@ -188,8 +234,7 @@ def attn_schemes(q, k, v, grid, candidates, mode, per_head: Sequence[float], sca
     """Head-wise schemes end to end: returns (o, scheme [B, H], agg [C, B, H])."""
     torch = _torch()
     p = problem_for(q, grid, candidates[0], scale, summarizer)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(t, name, q.shape, q.dtype)
+    _check_tensors([(q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype), (v, "v", q.shape, q.dtype)])
     bud = Budget(mode, per_head, window)
     n = spade_schemes_workspace_bytes(p, candidates, bud)
     if n == 0:

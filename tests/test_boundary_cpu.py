@@ -216,3 +216,66 @@ def test_empty_batch_is_a_noop():
 def test_status_strings():
     for s in range(5):
         assert spade.status_string(s).startswith("SPADE_")
+
+
+# ---------------------------------------------------------------------------
+# Python wrappers: every tensor's shape, dtype and length is checked before
+# any C call (forms before devices, so each check runs without a GPU)
+# ---------------------------------------------------------------------------
+
+def _cpu_problem(name="tiny_bf16"):
+    torch = pytest.importorskip("torch")
+    cfg = synth.get_config(name)
+    q = torch.zeros(cfg.B, cfg.H, cfg.N, cfg.d, dtype=torch.bfloat16)
+    g = oracle.Geometry(cfg.T, cfg.Hh, cfg.W, cfg.bt, cfg.bh, cfg.bw)
+    grid, block = (cfg.T, cfg.Hh, cfg.W), (cfg.bt, cfg.bh, cfg.bw)
+    return torch, cfg, g, q, grid, block
+
+
+def _raises(match, status, fn, *a, **kw):
+    with pytest.raises(spade.SpadeError, match=match) as ei:
+        fn(*a, **kw)
+    assert ei.value.status == status
+
+
+def test_estimate_select_checks_summaries():
+    torch, cfg, g, q, grid, block = _cpu_problem()
+    p = spade.problem_for(q, grid, block)
+    good = torch.zeros(cfg.B, cfg.H, g.nblk, cfg.d)
+    bud = ("count", [3] * cfg.H)
+    _raises("q_mean has shape", INVALID, spade.estimate_select, good[:, :, :-1], good, p, *bud)
+    _raises("k_mean has dtype", INVALID, spade.estimate_select, good, good.double(), p, *bud)
+    _raises("k_mean must be contiguous", INVALID, spade.estimate_select, good, good.transpose(2, 3).contiguous().transpose(2, 3), p, *bud)
+    _raises("q_mean must be a device tensor", INVALID, spade.estimate_select, good, good, p, *bud)
+    _raises("q_mean has shape", INVALID, spade.debug_scores, good[..., :8], good, p)
+
+
+def test_block_sparse_attn_checks_csr_and_output():
+    torch, cfg, g, q, grid, block = _cpu_problem()
+    R = cfg.B * cfg.H * g.nblk
+    rp = torch.zeros(R + 1, dtype=torch.int32)
+    ci = torch.zeros(4, dtype=torch.int32)
+    f = spade.block_sparse_attn
+    _raises("row_ptr has shape", INVALID, f, q, q, q, grid, block, rp[:-1], ci)
+    _raises("row_ptr has dtype", INVALID, f, q, q, q, grid, block, rp.long(), ci)
+    _raises("col_idx must be a one-dimensional", INVALID, f, q, q, q, grid, block, rp, ci.view(2, 2))
+    _raises("col_idx has dtype", INVALID, f, q, q, q, grid, block, rp, ci.float())
+    _raises("out has dtype", INVALID, f, q, q, q, grid, block, rp, ci, out=q.float())
+    _raises("out has shape", INVALID, f, q, q, q, grid, block, rp, ci, out=q[:, :1])
+    _raises("v has shape", INVALID, f, q, q, q[..., :32], grid, block, rp, ci)
+    _raises("q must be a device tensor", INVALID, f, q, q, q, grid, block, rp, ci)
+
+
+def test_attn_checks_workspace():
+    torch, cfg, g, q, grid, block = _cpu_problem()
+    p = spade.problem_for(q, grid, block)
+    need = spade.spade_workspace_bytes(p)
+    small = torch.zeros(need - 1, dtype=torch.uint8)
+    _raises("workspace has", CAP, spade.attn, q, q, q, grid, block, "count", [3] * cfg.H, workspace=small)
+    wrong = torch.zeros(need, dtype=torch.int8)
+    _raises("workspace has dtype", INVALID, spade.attn, q, q, q, grid, block, "count", [3] * cfg.H,
+            workspace=wrong)
+    _raises("workspace has shape", INVALID, spade.attn, q, q, q, grid, block, "count", [3] * cfg.H,
+            workspace=torch.zeros(2, need, dtype=torch.uint8))
+    _raises("q must be a device tensor", INVALID, spade.attn, q, q, q, grid, block, "count", [3] * cfg.H,
+            workspace=torch.zeros(need, dtype=torch.uint8))
