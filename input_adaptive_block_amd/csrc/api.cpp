@@ -210,7 +210,7 @@ Workspace workspace_layout(const Geom& g) {
   L.qpack = off; off = align256(off + pack);
   L.kpack = off; off = align256(off + pack);
   L.vpack = off; off = align256(off + pack);
-  L.queue = off; off = align256(off + (2 * kQueues + 2) * 4);
+  L.counter = off; off = align256(off + 4);
   L.total = off;
   return L;
 }
@@ -321,7 +321,7 @@ spade_status spade_block_sparse_attn(const spade_problem* p, const void* q, cons
     SPADE_TRY(dev(launch_summarize(g, true, q, k, v, nullptr, nullptr, qp, kp, vp, s)));
     return timed_attention(s, [&] {
       return launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o,
-                                reinterpret_cast<int*>(ws_ptr(workspace, L.queue)), num_cus(), s);
+                                reinterpret_cast<int*>(ws_ptr(workspace, L.counter)), num_cus(), s);
     });
   }
   return timed_attention(s, [&] {
@@ -356,7 +356,7 @@ spade_status spade_attn(const spade_problem* p, const void* q, const void* k, co
     SPADE_TRY(run_select(p, g, L, qm, km, budget, row_ptr, col_idx, workspace, s));
     return timed_attention(s, [&] {
       return launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o,
-                                reinterpret_cast<int*>(ws_ptr(workspace, L.queue)), num_cus(), s);
+                                reinterpret_cast<int*>(ws_ptr(workspace, L.counter)), num_cus(), s);
     });
   }
   SPADE_TRY(dev(launch_summarize(g, false, q, k, nullptr, qm, km, nullptr, nullptr, nullptr, s)));
@@ -379,16 +379,6 @@ spade_status spade_debug_scores(const spade_problem* p, const float* q_mean, con
   if (g.BH == 0) return SPADE_OK;
   if (!q_mean || !k_mean || !scores) return SPADE_ERR_INVALID_ARG;
   return dev(launch_scores(g, q_mean, k_mean, est_scale(p), scores, (hipStream_t)stream));
-}
-
-spade_status spade_debug_work_queues(const spade_problem* p, const int32_t* row_ptr, int64_t col_capacity,
-                                     int32_t* queue, void* stream) {
-  Geom g;
-  SPADE_TRY(make_geom(p, &g));
-  if (col_capacity < 0) return SPADE_ERR_INVALID_ARG;
-  if (g.R == 0) return SPADE_OK;
-  if (!row_ptr || !queue) return SPADE_ERR_INVALID_ARG;
-  return dev(launch_work_queues(g, row_ptr, col_capacity, queue, (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -528,7 +518,7 @@ spade_status spade_attn_schemes(const spade_problem* p, const void* q, const voi
       SPADE_TRY(dev(launch_summarize(g, true, q, k, v, qm, km, qp, kp, vp, s)));
       SPADE_TRY(run_select(p, g, W, qm, km, budget, row_ptr, col_idx, pw, s));
       SPADE_TRY(dev(launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, L.cap, scale, o,
-                                       reinterpret_cast<int*>(ws_ptr(pw, W.queue)), num_cus(), s)));
+                                       reinterpret_cast<int*>(ws_ptr(pw, W.counter)), num_cus(), s)));
     } else {
       SPADE_TRY(dev(launch_summarize(g, false, q, k, nullptr, qm, km, nullptr, nullptr, nullptr, s)));
       SPADE_TRY(run_select(p, g, W, qm, km, budget, row_ptr, col_idx, pw, s));

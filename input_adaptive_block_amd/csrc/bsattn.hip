@@ -16,12 +16,11 @@
 //   fetched once serves every row of the unit that keeps its block, which
 //   cuts L2 / Infinity-Cache traffic on video layers, where neighbouring rows
 //   keep mostly the same blocks.
-// * One persistent workgroup of 12 wavefronts per CU (three per SIMD) pulls
-//   units from eight contiguous queues (one per XCD, equal shares of kept
-//   blocks); a workgroup starts on queue blockIdx % 8 and steals from the next
-//   queues when its own is empty, so neighbouring Q blocks of a head share one
-//   XCD's L2.  With three wavefronts per SIMD, one wave's softmax runs beside
-//   the others' MFMAs.
+// * One persistent workgroup of 12 wavefronts per CU (three per SIMD) takes
+//   units from one atomic counter in (head, row) order, so the units in
+//   flight across the chip read the K/V of one or two heads, which stay in the
+//   Infinity Cache.  With three wavefronts per SIMD, one wave's softmax runs
+//   beside the others' MFMAs.
 // * Scores are computed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_bf16: each lane owns one query and 16 keys, so the row
 //   sum is in-lane plus one permlane32 swap at the end, the lazy-rescale test
@@ -93,66 +92,9 @@ __host__ __device__ inline UnitMap unit_map(const Geom& g) {
   return u;
 }
 
-// ---------------------------------------------------------------------------
-// work queues: eight contiguous unit ranges of about equal cost
-// ---------------------------------------------------------------------------
-constexpr int kQThreads = 1024;
-
-__device__ inline long long row_cost(const int* __restrict__ row_ptr, long long cap, int r) {
-  long long a = row_ptr[r], b = row_ptr[r + 1];
-  a = a < 0 ? 0 : (a > cap ? cap : a);
-  b = b < a ? a : (b > cap ? cap : b);
-  return b - a;
-}
-
-__global__ __launch_bounds__(kQThreads) void queue_kernel(Geom g, int U, const int* __restrict__ row_ptr,
-                                                          long long cap, int* __restrict__ queue) {
-  __shared__ long long part[kQThreads];
-  __shared__ int start[kQueues + 1];
-  const int tid = threadIdx.x;
-  const UnitMap um = unit_map(g);
-  if (tid <= kQueues) start[tid] = (tid == 0) ? 0 : U;
-  const int per = (U + kQThreads - 1) / kQThreads;
-  const int lo = min(U, tid * per), hi = min(U, lo + per);
-  // cost of a unit: kept blocks of each wave's row + 1
-  auto cost = [&](int u) -> long long {
-    const int bh = u / um.per_head, pi = u - bh * um.per_head;
-    long long c = 1;
-    for (int w = 0; w < kWaves; ++w) {
-      const int it = kWaves * pi + w;
-      if (it < um.items) c += row_cost(row_ptr, cap, bh * g.nblk + it / um.nsub);
-    }
-    return c;
-  };
-  long long s = 0;
-  for (int u = lo; u < hi; ++u) s += cost(u);
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < kQThreads; off <<= 1) {
-    const long long add = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  const long long total = part[kQThreads - 1];
-  long long run = part[tid] - s;  // exclusive prefix before unit lo
-  // exclusive prefix before the previous unit (-1 before unit 0)
-  long long prev = lo > 0 && lo < hi ? run - cost(lo - 1) : -1;
-  for (int u = lo; u < hi; ++u) {
-    // start[x] = first unit whose exclusive prefix reaches ceil(x * total / 8);
-    // exactly one unit satisfies this for each x, so the starts are ascending
-    // and the queues partition the units
-    for (int x = 1; x < kQueues; ++x) {
-      const long long t = (x * total + kQueues - 1) / kQueues;
-      if (run >= t && prev < t) start[x] = u;
-    }
-    prev = run;
-    run += cost(u);
-  }
-  __syncthreads();
-  if (tid <= kQueues) queue[tid] = start[tid];
-  if (tid < kQueues) queue[kQueues + 1 + tid] = 0;  // cursors
-}
+// the attention kernel's unit counter, cleared on the launch stream before
+// each launch (a kernel, so that the launch sequence can be captured)
+__global__ void counter_reset_kernel(int* __restrict__ counter) { *counter = 0; }
 
 // ---------------------------------------------------------------------------
 // bf16 attention
@@ -209,7 +151,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     Geom g, const uint16_t* __restrict__ qpack, const uint16_t* __restrict__ kpack,
     const uint16_t* __restrict__ vpack, const int* __restrict__ row_ptr, const int* __restrict__ col_idx,
-    long long cap, float scale_log2, uint16_t* __restrict__ out, int* __restrict__ queue, int U) {
+    long long cap, float scale_log2, uint16_t* __restrict__ out, int* __restrict__ counter, int U) {
   constexpr int SUB = 32 * D;                  // bf16 elements of one 32-key subtile
   constexpr int STAGE_KB = 2 * SUB * 2 / 1024;  // 1 KB copies per tensor per stage (2 subtiles)
   constexpr int CPW = STAGE_KB / kCopyWaves;   // copies per copying wave per tensor
@@ -235,25 +177,11 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: row-mask tests stay scalar
   const int half = lane >> 5;
   const UnitMap um = unit_map(g);
-  const int* qstart = queue;
-  int* qcursor = queue + kQueues + 1;
-  int qx = blockIdx.x % kQueues;
-  int visited = 0;
 
   for (;;) {
     if (tid == 0) {
-      int unit = -1;
-      while (visited < kQueues) {
-        const int n = qstart[qx + 1] - qstart[qx];
-        const int it = n > 0 ? atomicAdd(&qcursor[qx], 1) : 0;
-        if (it < n) {
-          unit = qstart[qx] + it;
-          break;
-        }
-        ++visited;
-        qx = (qx + 1) % kQueues;
-      }
-      s_unit = unit;
+      const int unit = atomicAdd(counter, 1);
+      s_unit = unit < U ? unit : -1;
     }
     __syncthreads();
     const int unit = s_unit;
@@ -666,21 +594,13 @@ __global__ __launch_bounds__(kF32Threads) void bsattn_f32_kernel(
 
 }  // namespace
 
-hipError_t launch_work_queues(const Geom& g, const int* row_ptr, long long col_capacity, int* queue,
-                              hipStream_t s) {
-  if (g.R == 0) return hipSuccess;
-  const int U = g.BH * unit_map(g).per_head;
-  queue_kernel<<<1, kQThreads, 0, s>>>(g, U, row_ptr, col_capacity, queue);
-  return hipGetLastError();
-}
-
 hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpack, const void* vpack,
                               const int* row_ptr, const int* col_idx, long long col_capacity, float scale,
-                              void* o, int* queue, int num_cus, hipStream_t s) {
+                              void* o, int* counter, int num_cus, hipStream_t s) {
   if (g.R == 0) return hipSuccess;
   const UnitMap um = unit_map(g);
   const int U = g.BH * um.per_head;
-  queue_kernel<<<1, kQThreads, 0, s>>>(g, U, row_ptr, col_capacity, queue);
+  counter_reset_kernel<<<1, 1, 0, s>>>(counter);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int grid = num_cus;  // one 12-wave workgroup per CU (LDS-limited)
@@ -690,11 +610,11 @@ hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpac
   if (g.d == 128)
     bsattn_bf16_kernel<128><<<grid, kThreads, 0, s>>>(
         g, (const uint16_t*)qpack, (const uint16_t*)kpack, (const uint16_t*)vpack, row_ptr, col_idx,
-        col_capacity, scale_log2, (uint16_t*)o, queue, U);
+        col_capacity, scale_log2, (uint16_t*)o, counter, U);
   else
     bsattn_bf16_kernel<64><<<grid, kThreads, 0, s>>>(
         g, (const uint16_t*)qpack, (const uint16_t*)kpack, (const uint16_t*)vpack, row_ptr, col_idx,
-        col_capacity, scale_log2, (uint16_t*)o, queue, U);
+        col_capacity, scale_log2, (uint16_t*)o, counter, U);
   return hipGetLastError();
 }
 

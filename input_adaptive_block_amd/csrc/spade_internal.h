@@ -10,7 +10,6 @@ namespace spade {
 constexpr int kMaxHeads = 256;     // per-head budgets travel as kernel arguments
 constexpr int kMaxBlocks = 4096;   // nblk limit (selection keeps a row in registers)
 constexpr int kMaxBlockTokens = 1024;
-constexpr int kQueues = 8;         // one work queue per XCD of the MI355X
 
 // Geometry of one problem, valid on host and device.
 struct Geom {
@@ -85,7 +84,7 @@ struct Workspace {
   size_t qpack;     // bf16 [BH * nblk * P * d]
   size_t kpack;
   size_t vpack;
-  size_t queue;     // int32 [2 * kQueues + 2]
+  size_t counter;   // int32: the attention kernel's unit counter
   size_t total;
   int mask_words;
 };
@@ -112,13 +111,9 @@ hipError_t launch_select(const Geom& g, const double* scores, const SelectArgs& 
 hipError_t launch_scan(const Geom& g, const int* counts, int* row_ptr, hipStream_t s);
 hipError_t launch_compact(const Geom& g, const int* row_ptr, const uint32_t* mask, int mask_words,
                           int* col_idx, hipStream_t s);
-// The attention kernel's work queues for a CSR (start of each queue's unit
-// range, then the cursors), as its launch builds them.
-hipError_t launch_work_queues(const Geom& g, const int* row_ptr, long long col_capacity, int* queue,
-                              hipStream_t s);
 hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpack, const void* vpack,
                               const int* row_ptr, const int* col_idx, long long col_capacity,
-                              float scale, void* o, int* queue, int num_cus, hipStream_t s);
+                              float scale, void* o, int* counter, int num_cus, hipStream_t s);
 hipError_t launch_bsattn_f32(const Geom& g, const float* q, const float* k, const float* v,
                              const int* row_ptr, const int* col_idx, long long col_capacity,
                              float scale, float* o, hipStream_t s);

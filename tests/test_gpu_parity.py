@@ -387,54 +387,6 @@ def test_block_sparse_attn_on_oracle_csr(name):
     assert err <= (BF16_TOL if cfg.dtype == "bf16" else F32_TOL), err
 
 
-def expected_work_queues(cfg, rp):
-    """The attention kernel's queue partition, restated: units are 12
-    consecutive (row, 32-query subtile) items of a head; a unit costs 1 + the
-    kept blocks of each item's row; queue x starts at the first unit whose
-    exclusive cost prefix reaches ceil(x * total / 8)."""
-    g = geom(cfg)
-    ntok = max(len(t) for t in oracle.block_tokens(g))
-    nsub = (ntok + 31) // 32
-    items = g.nblk * nsub
-    per_head = (items + 11) // 12
-    kept = np.diff(rp)
-    cost = []
-    for bh in range(cfg.B * cfg.H):
-        for pi in range(per_head):
-            its = range(12 * pi, min(items, 12 * pi + 12))
-            cost.append(1 + sum(int(kept[bh * g.nblk + it // nsub]) for it in its))
-    cost = np.array(cost, dtype=np.int64)
-    U = len(cost)
-    pre = np.concatenate([[0], np.cumsum(cost)])
-    total = int(pre[-1])
-    starts = [0]
-    for x in range(1, 8):
-        t = (x * total + 7) // 8
-        hit = np.nonzero(pre[:U] >= t)[0]
-        starts.append(int(hit[0]) if len(hit) else U)
-    return starts + [U], cost
-
-
-@pytest.mark.parametrize("name", ["tiny", "ragged_p64", "mid_shape", "small_shape", "ragged_small", "big_block",
-                                  "token_level", "max_blocks", "max_block_tokens"])
-def test_work_queues_partition_the_units(name):
-    """Integer work, checked bit for bit: the eight queue ranges are the
-    restated partition, ascending, and cover every unit exactly once."""
-    cfg = synth.get_config(name)
-    x = synth.make_inputs(cfg)
-    o, rp, ci = run_attn(cfg, x)
-    grid, block = grid_block(cfg)
-    p = spade.problem_for(to_dev(cfg, x["q"]), grid, block)
-    queue = torch.full((18,), -7, dtype=torch.int32, device="cuda")
-    spade.spade_debug_work_queues(p, rp, ci.numel(), queue)
-    torch.cuda.synchronize()
-    got = queue.cpu().numpy()
-    want, cost = expected_work_queues(cfg, rp.cpu().numpy().astype(np.int64))
-    assert got[:9].tolist() == want, (got[:9].tolist(), want)
-    assert (np.diff(got[:9]) >= 0).all() and got[0] == 0 and got[8] == len(cost)
-    assert (got[9:17] == 0).all()  # the cursors (entry 17 is unused)
-
-
 @pytest.mark.parametrize("name", ["mid_shape", "tiny"])
 def test_arbitrary_csr_is_memory_safe(name):
     """A row is a set (repeated ids count once, order is free), invalid ids are
