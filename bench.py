@@ -125,17 +125,34 @@ def cpu_baseline(cfg, x, seconds):
         if done:
             break
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    host_cores = len(os.sched_getaffinity(0))
     return {
         "value": float(flops / dt / 1e12),
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        # the oracle's numpy kernels run on the BLAS pool; everything else is
+        # one Python thread
+        "cores": int(min(blas, host_cores)),
+        "host_cores": int(host_cores),
+        "blas_threads": int(blas),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"the workload's first {heads} head(s) in order: fp64 summaries, scores and selection, "
                    f"then block-sparse attention of {rows} Q-block rows ({flops / 1e9:.1f} GFLOP "
-                   f"in {dt:.1f} s, BLAS threads {threads})"),
+                   f"in {dt:.1f} s)"),
         "seconds": float(dt),
     }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():

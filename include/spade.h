@@ -157,11 +157,14 @@ spade_status spade_summarize_sics(const spade_problem* p, const void* q, const v
                                   float* q_mean, float* k_mean, float* q_sics, float* k_sics,
                                   void* stream);
 
-/* Estimator + index search: S_ij = scale * <q_mean_i, k_mean_j> in fp64, then
- * per row the blocks in (S descending, j ascending) order are kept by the
- * budget.  Writes row_ptr [R+1] and col_idx (ascending ids per row).
- * col_capacity (entries) must be >= spade_max_nnz.  Workspace as given by
- * spade_workspace_bytes. */
+/* Estimator + index search (the author-page abstracts on catalyzex.com: the
+ * executor's low-overhead index search; gist.science technical summary,
+ * "Methodology 1. vDiT-SSR", Summarizer & Estimator Expressions: the
+ * inter-block importance score decides which blocks each Q block retains):
+ * S_ij = scale * <q_mean_i, k_mean_j> in fp64, then per row the blocks in
+ * (S descending, j ascending) order are kept by the budget.  Writes row_ptr
+ * [R+1] and col_idx (ascending ids per row).  col_capacity (entries) must be
+ * >= spade_max_nnz.  Workspace as given by spade_workspace_bytes. */
 spade_status spade_estimate_select(const spade_problem* p, const float* q_mean, const float* k_mean,
                                    const spade_budget* budget, int32_t* row_ptr, int32_t* col_idx,
                                    int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream);
@@ -177,8 +180,13 @@ spade_status spade_block_sparse_attn(const spade_problem* p, const void* q, cons
                                      const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
                                      void* o, void* workspace, size_t ws_bytes, void* stream);
 
-/* The whole path: summarize -> estimate/select -> block-sparse attention.
- * Also returns the CSR it used in row_ptr / col_idx (capacity as above). */
+/* The whole path of the executor (the catalyzex.com abstracts: index search,
+ * flash block-sparse attention and kernel grouping; gist.science technical
+ * summary, "Methodology 3. Head-wise Sparse Attention Execution"): the fused
+ * blocking + summaries (Kernel Fusion) -> estimate/select -> block-sparse
+ * attention, all heads in one launch per step (Head Grouping), on one stream
+ * with no host synchronisation.  Also returns the CSR it used in row_ptr /
+ * col_idx (capacity as above). */
 spade_status spade_attn(const spade_problem* p, const void* q, const void* k, const void* v,
                         const spade_budget* budget, void* o, int32_t* row_ptr, int32_t* col_idx,
                         int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream);

@@ -13,7 +13,9 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libspade.so")
+# SPADE_LIB names another build of the same library (the host-sanitizer
+# build the CPU tests load); by default the in-tree libspade.so
+LIB_PATH = os.environ.get("SPADE_LIB") or os.path.join(_PKG, "libspade.so")
 
 SPADE_OK = 0
 SPADE_ERR_INVALID_ARG = 1

@@ -23,9 +23,20 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# host-side AddressSanitizer + UndefinedBehaviorSanitizer (device code is
+# built as usual): a CPU-test build of the library's host validation, sizing
+# and launch code, loaded with SPADE_LIB and the ASan runtime preloaded
+SANITIZE = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libspade_asan.so")
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    out_dir = ASAN_DIR if sanitize else BUILD
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    flags = [f for f in FLAGS if f != "-O3"] + SANITIZE if sanitize else FLAGS
+    cmd = [HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -34,22 +45,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path.
+    sanitize=True builds the host-sanitizer variant at ASAN_LIB instead."""
+    os.makedirs(ASAN_DIR if sanitize else BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
+        objs = list(ex.map(lambda f: _compile(f, sanitize), SOURCES))
+    lib = ASAN_LIB if sanitize else LIB
+    tmp = lib + ".tmp"
+    extra = ["-shared-libasan", "-fsanitize=address,undefined"] if sanitize else []
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, sanitize="--sanitize" in sys.argv)
     sys.exit(0)
