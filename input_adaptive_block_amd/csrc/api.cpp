@@ -182,13 +182,18 @@ char* ws_ptr(void* ws, size_t off) { return reinterpret_cast<char*>(ws) + off; }
 spade_status run_select(const spade_problem* p, const Geom& g, const Workspace& L, const float* qm,
                         const float* km, const spade_budget* bgt, int* row_ptr, int* col_idx, void* ws,
                         hipStream_t s) {
-  double* scores = reinterpret_cast<double*>(ws_ptr(ws, L.scores));
   int* counts = reinterpret_cast<int*>(ws_ptr(ws, L.counts));
   uint32_t* mask = reinterpret_cast<uint32_t*>(ws_ptr(ws, L.mask));
-  SPADE_TRY(dev(launch_scores(g, qm, km, est_scale(p), scores, s)));
   const SelectArgs a = make_select_args(bgt, g);
-  SPADE_TRY(dev(launch_select(g, scores, a, counts, mask, L.mask_words, s)));
-  SPADE_TRY(dev(launch_scan(g, counts, row_ptr, s)));
+  if (fused_select_fits(g)) {
+    // scores of a row tile stay in LDS
+    SPADE_TRY(dev(launch_estimate_select(g, qm, km, est_scale(p), a, counts, mask, L.mask_words, s)));
+  } else {
+    double* scores = reinterpret_cast<double*>(ws_ptr(ws, L.scores));
+    SPADE_TRY(dev(launch_scores(g, qm, km, est_scale(p), scores, s)));
+    SPADE_TRY(dev(launch_select(g, scores, a, counts, mask, L.mask_words, s)));
+  }
+  SPADE_TRY(dev(launch_scan(g, counts, row_ptr, reinterpret_cast<int*>(ws_ptr(ws, L.scan)), s)));
   SPADE_TRY(dev(launch_compact(g, row_ptr, mask, L.mask_words, col_idx, s)));
   return SPADE_OK;
 }
@@ -201,7 +206,9 @@ Workspace workspace_layout(const Geom& g) {
   L.mask_words = (g.nblk + 31) / 32;
   L.counts = off; off = align256(off + (size_t)g.R * 4);
   L.mask = off; off = align256(off + (size_t)g.R * L.mask_words * 4);
-  L.scores = off; off = align256(off + (size_t)g.R * g.nblk * 8);
+  // fp64 scores in HBM only for rows wider than the fused kernel's LDS tile
+  L.scores = off; off = align256(off + (fused_select_fits(g) ? 0 : (size_t)g.R * g.nblk * 8));
+  L.scan = off; off = align256(off + ((size_t)scan_chunks(g.R) + 1) * 4);
   L.qmean = off; off = align256(off + (size_t)g.BH * g.nblk * g.d * 4);
   L.kmean = off; off = align256(off + (size_t)g.BH * g.nblk * g.d * 4);
   // packed tiles plus two spare 32-row subtiles: the attention kernel copies
@@ -296,7 +303,7 @@ spade_status spade_estimate_select(const spade_problem* p, const float* q_mean, 
   const Workspace L = workspace_layout(g);
   if (ws_bytes < L.total) return SPADE_ERR_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
-  if (g.R == 0) return dev(launch_scan(g, nullptr, row_ptr, s));
+  if (g.R == 0) return dev(launch_scan(g, nullptr, row_ptr, nullptr, s));
   if (!q_mean || !k_mean || !col_idx || !workspace) return SPADE_ERR_INVALID_ARG;
   return run_select(p, g, L, q_mean, k_mean, budget, row_ptr, col_idx, workspace, s);
 }
@@ -343,7 +350,7 @@ spade_status spade_attn(const spade_problem* p, const void* q, const void* k, co
   if (ws_bytes < L.total) return SPADE_ERR_CAPACITY;
   if (!row_ptr) return SPADE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if (g.R == 0) return dev(launch_scan(g, nullptr, row_ptr, s));
+  if (g.R == 0) return dev(launch_scan(g, nullptr, row_ptr, nullptr, s));
   if (!q || !k || !v || !o || !col_idx || !workspace) return SPADE_ERR_INVALID_ARG;
   float* qm = reinterpret_cast<float*>(ws_ptr(workspace, L.qmean));
   float* km = reinterpret_cast<float*>(ws_ptr(workspace, L.kmean));

@@ -7,14 +7,19 @@
 // feeds the result to the attention kernel as a block-sparse row format.
 //
 // Stages (all on the caller's stream, no host synchronization):
-//   scores_kernel   S = scale * qbar kbar^T per head in fp64 on
-//                   v_mfma_f64_16x16x4_f64 (summaries are fp32, exact in fp64).
-//   select_kernel   one wavefront per row.  The row lives in registers as
-//                   64-bit order keys; a bitwise threshold search (64 rounds of
-//                   ballots or masked fp64 sums) finds the k-th key (count /
-//                   ratio) or the mass cut (mass), ties go to the lower block
-//                   id.  Emits the kept set as a bitmask and a count.
-//   scan_kernel     row_ptr = exclusive prefix sum of the counts.
+//   estimate_select_kernel
+//                   one workgroup per tile of 16 rows of a head: their fp64
+//                   scores S = scale * qbar kbar^T on v_mfma_f64_16x16x4_f64
+//                   (summaries are fp32, their products exact in fp64) go into
+//                   LDS, never to HBM; then one wavefront per row holds the row
+//                   in registers as 64-bit order keys and a bitwise threshold
+//                   search (ballots or masked fp64 sums, per bit from the top)
+//                   finds the k-th key (count / ratio) or the mass cut (mass),
+//                   ties to the lower block id.  Emits the kept set as a
+//                   bitmask and a count.  Rows wider than the LDS tile take
+//                   scores_kernel (S in HBM) + select_kernel, same arithmetic.
+//   chunk_sum / chunk_offsets / scan_apply
+//                   row_ptr = exclusive prefix sum of the counts, over chunks.
 //   compact_kernel  one wavefront per row writes the kept ids ascending.
 #include "spade_internal.h"
 
@@ -26,60 +31,72 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // scores
 // ---------------------------------------------------------------------------
-constexpr int kSRows = 32, kSCols = 64;
 
-template <int D>
-__global__ __launch_bounds__(256) void scores_kernel(Geom g, const float* __restrict__ qm,
-                                                     const float* __restrict__ km, double scale,
-                                                     double* __restrict__ S) {
-  constexpr int LD = D + 4;
-  __shared__ __attribute__((aligned(16))) float qs[kSRows * LD];
-  __shared__ __attribute__((aligned(16))) float ks[kSCols * LD];
-  const int bh = blockIdx.z;
-  if (!head_active(g, bh)) return;  // another scheme's head (whole workgroup)
-  const int row0 = blockIdx.x * kSRows, col0 = blockIdx.y * kSCols;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nb = g.nblk;
-  const float* qh = qm + (size_t)bh * nb * D;
-  const float* kh = km + (size_t)bh * nb * D;
-  // 16-byte loads and stores (rows of D floats; the LDS row stride D + 4
-  // keeps every row 16-byte aligned)
-  constexpr int V = D / 4;
-  for (int t = tid; t < kSRows * V; t += 256) {
-    const int r = t / V, c = 4 * (t - r * V);
-    const float4 x = (row0 + r < nb) ? *reinterpret_cast<const float4*>(qh + (size_t)(row0 + r) * D + c)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(&qs[r * LD + c]) = x;
-  }
-  for (int t = tid; t < kSCols * V; t += 256) {
-    const int r = t / V, c = 4 * (t - r * V);
-    const float4 x = (col0 + r < nb) ? *reinterpret_cast<const float4*>(kh + (size_t)(col0 + r) * D + c)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(&ks[r * LD + c]) = x;
-  }
-  __syncthreads();
-  const int wr = wave >> 1, wc = wave & 1;
-  f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+// 16 x 16 tiles of S / scale: rows row0 .. row0 + 15 and columns
+// 16 ct .. 16 ct + 15 of one head, on v_mfma_f64_16x16x4_f64.  At k-step s
+// lane (li, lk) feeds channel lk D/4 + s of row li (A) and of column li (B):
+// a permutation of the channels that lets each lane read its D/4 channels of
+// a summary as contiguous 16-byte loads.  The fp32 summaries' products are
+// exact in fp64; rows or columns past nK repeat the last one (never stored).
+// A wave keeps its rows' operands in registers for all of its tiles.
+// f(ct, acc) receives each tile's result: D[lk + 4 v][li] in lane (lk, li),
+// register v.
+template <int D, class F>
+__device__ inline void score_tiles(const float* __restrict__ qh, const float* __restrict__ kh, int nK, int row0,
+                                   int ct0, int step, int lane, F f) {
+  constexpr int NS = D / 4;  // k-steps
+  constexpr int NV = NS / 4; // float4 loads per operand
   const int li = lane & 15, lk = lane >> 4;
-#pragma unroll 4
-  for (int s = 0; s < D / 4; ++s) {
-    const double a = (double)qs[(16 * wr + li) * LD + 4 * s + lk];
-    const double b0 = (double)ks[(32 * wc + li) * LD + 4 * s + lk];
-    const double b1 = (double)ks[(32 * wc + 16 + li) * LD + 4 * s + lk];
-    acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b0, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b1, acc1, 0, 0, 0);
-  }
-  double* Sh = S + (size_t)bh * nb * nb;
-  // v_mfma_f64_16x16x4_f64 leaves D[lk + 4 v][li] in lane (lk, li), register v
+  const int ntiles = (nK + 15) / 16;
+  if (ct0 >= ntiles) return;
+  float4 qa[NV], kb[NV];
+  const float4* qrow = reinterpret_cast<const float4*>(qh + (size_t)min(row0 + li, nK - 1) * D + lk * NS);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int i = row0 + 16 * wr + lk + 4 * v;
-    const int j0 = col0 + 32 * wc + li, j1 = j0 + 16;
-    if (i < nb) {
-      if (j0 < nb) Sh[(size_t)i * nb + j0] = scale * acc0[v];
-      if (j1 < nb) Sh[(size_t)i * nb + j1] = scale * acc1[v];
+  for (int v = 0; v < NV; ++v) qa[v] = qrow[v];
+  for (int ct = ct0; ct < ntiles; ct += step) {
+    const float4* krow = reinterpret_cast<const float4*>(kh + (size_t)min(16 * ct + li, nK - 1) * D + lk * NS);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) kb[v] = krow[v];
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[v].x, (double)kb[v].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[v].y, (double)kb[v].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[v].z, (double)kb[v].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[v].w, (double)kb[v].w, acc, 0, 0, 0);
     }
+    f(ct, acc);
   }
+}
+
+constexpr int kFRows = 16;   // selection rows per workgroup (one row tile)
+constexpr int kFWaves = 8;   // waves per workgroup
+
+// S = scale * qbar kbar^T written to HBM, one row tile per workgroup (rows
+// wider than the fused kernel's LDS tile, and the scores test hook).  The
+// same arithmetic as the fused kernel, bit for bit.
+template <int D>
+__global__ __launch_bounds__(64 * kFWaves) void scores_kernel(Geom g, const float* __restrict__ qm,
+                                                              const float* __restrict__ km, double scale,
+                                                              double* __restrict__ S) {
+  const int bh = blockIdx.y;
+  if (!head_active(g, bh)) return;  // another scheme's head (whole workgroup)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nK = g.nblk;
+  const int row0 = blockIdx.x * kFRows;
+  const float* qh = qm + (size_t)bh * nK * D;
+  const float* kh = km + (size_t)bh * nK * D;
+  double* Sh = S + (size_t)bh * nK * nK;
+  const int li = lane & 15, lk = lane >> 4;
+  score_tiles<D>(qh, kh, nK, row0, wave, kFWaves, lane, [&](int ct, const f64x4& acc) {
+    const int j = 16 * ct + li;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = row0 + lk + 4 * v;
+      if (i < nK && j < nK) Sh[(size_t)i * nK + j] = scale * acc[v];
+    }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -124,18 +141,66 @@ __device__ inline uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// One lane-exchange step of a butterfly over the wavefront for a double:
+// DPP within a 16-lane row (CTRL: quad_perm [1,0,3,2] = xor 1, quad_perm
+// [2,3,0,1] = xor 2, row_half_mirror, row_mirror), then v_permlane16_swap and
+// v_permlane32_swap across rows.  After xor 1 and xor 2 every lane of a quad
+// holds the same bits, so the mirrors meet the same partner values as xor 4
+// and xor 8 would, and the swaps those of xor 16 and xor 32: the steps add
+// the same operand pairs as a shuffle-xor butterfly, every lane ending with
+// the same bits, at VALU latency instead of LDS-permute latency.
+template <int CTRL>
+__device__ inline double dpp_f64(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// The two values a permlane swap leaves a lane: its own and its partner's
+// (xor 16 for SWAP16, xor 32 otherwise), in either order.
+template <bool SWAP16>
+__device__ inline void swap_f64(double x, double& a, double& b) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  const auto sl = SWAP16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                         : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto sh = SWAP16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                         : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  a = __builtin_bit_cast(double, ((uint64_t)sh[0] << 32) | sl[0]);
+  b = __builtin_bit_cast(double, ((uint64_t)sh[1] << 32) | sl[1]);
+}
+
 __device__ inline double wave_sum(double x) {
-  // butterfly: every lane ends with the same bits (each step adds the same
-  // pair of operands, only in swapped order)
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
-  return x;
+  x += dpp_f64<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f64<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f64<0x141>(x);  // row_half_mirror
+  x += dpp_f64<0x140>(x);  // row_mirror
+  double a, b;
+  swap_f64<true>(x, a, b);
+  x = a + b;
+  swap_f64<false>(x, a, b);
+  return a + b;
 }
 
 __device__ inline double wave_max(double x) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x = fmax(x, __shfl_xor(x, off));
-  return x;
+  x = fmax(x, dpp_f64<0xB1>(x));
+  x = fmax(x, dpp_f64<0x4E>(x));
+  x = fmax(x, dpp_f64<0x141>(x));
+  x = fmax(x, dpp_f64<0x140>(x));
+  double a, b;
+  swap_f64<true>(x, a, b);
+  x = fmax(a, b);
+  swap_f64<false>(x, a, b);
+  return fmax(a, b);
+}
+
+// lane l's double (l uniform)
+__device__ inline double read_lane_f64(double x, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // The bitwise threshold searches below fix the threshold's bits from the
@@ -155,45 +220,28 @@ __device__ inline bool isolated_threshold(const uint64_t (&key)[E], int bit, uin
     const uint64_t b = __ballot((key[e] & hi) == T);
     if (b != 0ull) {
       const int l = __builtin_ctzll(b);
-      const uint32_t lo32 = __shfl((uint32_t)key[e], l), hi32 = __shfl((uint32_t)(key[e] >> 32), l);
+      const uint32_t lo32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[e], l);
+      const uint32_t hi32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key[e] >> 32), l);
       T = ((uint64_t)hi32 << 32) | lo32;
     }
   }
   return true;
 }
 
+// The score an order key encodes (order_key is a bijection on doubles).
+__device__ inline double key_score(uint64_t k) {
+  const uint64_t u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __longlong_as_double((long long)u);
+}
+
+// Selection of one row whose scores S are held by the wave as E order keys
+// per lane (block 64 e + lane in key[e], 0 past nK): the kept set as a
+// bitmask row and its count.
 template <int E>
-__global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __restrict__ S, SelectArgs a,
-                                                     int* __restrict__ counts, uint32_t* __restrict__ mask,
-                                                     int mask_words) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= g.R) return;  // whole wave exits together
+__device__ inline void select_row(const Geom& g, const SelectArgs& a, int row, int lane, uint64_t (&key)[E],
+                                  int* __restrict__ counts, uint32_t* __restrict__ mask, int mask_words) {
   const int nK = g.nblk;
   const int h = (row / nK) % g.H;
-  if (!head_active(g, row / nK)) {
-    // another scheme's head: an empty row (its scores were never computed)
-    uint32_t* mrow = mask + (size_t)row * mask_words;
-    for (int w = lane; w < mask_words; w += 64) mrow[w] = 0u;
-    if (lane == 0) counts[row] = 0;
-    return;
-  }
-  const double* Sr = S + (size_t)row * nK;
-
-  uint64_t key[E];
-  double sv[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = 64 * e + lane;
-    if (j < nK) {
-      sv[e] = Sr[j];
-      key[e] = order_key(sv[e]);
-    } else {
-      sv[e] = -__builtin_huge_val();
-      key[e] = 0ull;  // below every real score
-    }
-  }
-
   bool kept[E];
   if (a.mode != 2) {
     // ---- count / ratio: the k-th largest key, ties to the lower id ----
@@ -221,15 +269,15 @@ __global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __res
     }
   } else {
     // ---- mass: shortest (S desc, id asc) prefix with softmax mass >= tau ----
-    double mx = sv[0];
+    uint64_t kmax = key[0];
 #pragma unroll
-    for (int e = 1; e < E; ++e) mx = fmax(mx, sv[e]);
-    mx = wave_max(mx);
+    for (int e = 1; e < E; ++e) kmax = key[e] > kmax ? key[e] : kmax;
+    const double mx = wave_max(key_score(kmax));  // lane 0 always holds a real key
     double p[E];
     double loc = 0.0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      p[e] = (64 * e + lane < nK) ? exp_nonpos(sv[e] - mx) : 0.0;
+      p[e] = (64 * e + lane < nK) ? exp_nonpos(key_score(key[e]) - mx) : 0.0;
       loc += p[e];
     }
     const double Z = wave_sum(loc);
@@ -260,7 +308,7 @@ __global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __res
         tie &= tie - 1;
         if (cum < target || (cum == 0.0 && target == 0.0)) {
           if (lane == l) kept[e] = true;
-          cum += __shfl(p[e], l);
+          cum += read_lane_f64(p[e], l);
         }
       }
     }
@@ -283,17 +331,96 @@ __global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __res
   }
 
   int cnt = 0;
+  uint32_t* mrow = mask + (size_t)row * mask_words;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint64_t bits = __ballot(kept[e]);
     cnt += __popcll(bits);
     if (lane == 0) {
-      uint32_t* mrow = mask + (size_t)row * mask_words;
       if (2 * e < mask_words) mrow[2 * e] = (uint32_t)bits;
       if (2 * e + 1 < mask_words) mrow[2 * e + 1] = (uint32_t)(bits >> 32);
     }
   }
   if (lane == 0) counts[row] = cnt;
+}
+
+// An empty row (another scheme's head: its scores were never computed).
+__device__ inline void empty_row(int row, int lane, int* __restrict__ counts, uint32_t* __restrict__ mask,
+                                 int mask_words) {
+  uint32_t* mrow = mask + (size_t)row * mask_words;
+  for (int w = lane; w < mask_words; w += 64) mrow[w] = 0u;
+  if (lane == 0) counts[row] = 0;
+}
+
+// One wavefront per row, the row's fp64 scores read from HBM (rows wider than
+// the fused kernel's LDS tile).
+template <int E>
+__global__ __launch_bounds__(256) void select_kernel(Geom g, const double* __restrict__ S, SelectArgs a,
+                                                     int* __restrict__ counts, uint32_t* __restrict__ mask,
+                                                     int mask_words) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= g.R) return;  // whole wave exits together
+  const int nK = g.nblk;
+  if (!head_active(g, row / nK)) {
+    empty_row(row, lane, counts, mask, mask_words);
+    return;
+  }
+  const double* Sr = S + (size_t)row * nK;
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = 64 * e + lane;
+    key[e] = j < nK ? order_key(Sr[j]) : 0ull;  // below every real score
+  }
+  select_row<E>(g, a, row, lane, key, counts, mask, mask_words);
+}
+
+// ---------------------------------------------------------------------------
+// fused estimate + select: one row tile's fp64 scores in LDS
+// ---------------------------------------------------------------------------
+
+// The workgroup's 16 rows of S (score_tile over every column tile, wave w
+// taking tiles w, w + 8, ...) go into LDS, then each wave selects its rows
+// straight from there: S is never written to HBM.
+template <int D, int E>
+__global__ __launch_bounds__(64 * kFWaves) __attribute__((amdgpu_waves_per_eu(4, 4))) void estimate_select_kernel(Geom g, const float* __restrict__ qm,
+                                                                        const float* __restrict__ km, double scale,
+                                                                        SelectArgs a, int* __restrict__ counts,
+                                                                        uint32_t* __restrict__ mask,
+                                                                        int mask_words) {
+  constexpr int NB = 64 * E;  // widest row the tile holds
+  __shared__ double St[kFRows * NB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nK = g.nblk;
+  const int bh = blockIdx.y;
+  const int row0 = blockIdx.x * kFRows;  // first Q block of the tile
+  if (!head_active(g, bh)) {
+    for (int r = wave; r < kFRows && row0 + r < nK; r += kFWaves)
+      empty_row(bh * nK + row0 + r, lane, counts, mask, mask_words);
+    return;
+  }
+  const float* qh = qm + (size_t)bh * nK * D;
+  const float* kh = km + (size_t)bh * nK * D;
+  const int li = lane & 15, lk = lane >> 4;
+  score_tiles<D>(qh, kh, nK, row0, wave, kFWaves, lane, [&](int ct, const f64x4& acc) {
+    const int j = 16 * ct + li;
+    if (j < nK) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) St[(lk + 4 * v) * NB + j] = scale * acc[v];
+    }
+  });
+  __syncthreads();
+  for (int r = wave; r < kFRows && row0 + r < nK; r += kFWaves) {
+    uint64_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = 64 * e + lane;
+      key[e] = j < nK ? order_key(St[r * NB + j]) : 0ull;  // below every real score
+    }
+    select_row<E>(g, a, bh * nK + row0 + r, lane, key, counts, mask, mask_words);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -347,32 +474,83 @@ __global__ __launch_bounds__(256) void scheme_choose_kernel(int BH, int C, const
 // ---------------------------------------------------------------------------
 // CSR
 // ---------------------------------------------------------------------------
-constexpr int kScanThreads = 1024;
+// row_ptr in three passes over chunks of kScanChunk rows: each chunk's sum,
+// an exclusive scan of the chunk sums (one workgroup), then each chunk's
+// exclusive scan plus its offset.
+constexpr int kScanThreads = 256;
+constexpr int kScanPer = kScanChunk / kScanThreads;  // rows per thread
 
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(int R, const int* __restrict__ counts,
-                                                            int* __restrict__ row_ptr) {
-  __shared__ int part[kScanThreads];
+__device__ inline int block_exclusive_scan(int x, int* part) {
+  // exclusive prefix of x over the workgroup (kScanThreads threads)
   const int tid = threadIdx.x;
-  const int per = (R + kScanThreads - 1) / kScanThreads;
-  const int lo = min(R, tid * per), hi = min(R, lo + per);
-  int s = 0;
-  for (int r = lo; r < hi; ++r) s += counts[r];
-  part[tid] = s;
+  part[tid] = x;
   __syncthreads();
-  // Hillis-Steele inclusive scan over the per-thread sums
   for (int off = 1; off < kScanThreads; off <<= 1) {
     const int add = tid >= off ? part[tid - off] : 0;
     __syncthreads();
     part[tid] += add;
     __syncthreads();
   }
+  return part[tid] - x;
+}
+
+__global__ __launch_bounds__(kScanThreads) void chunk_sum_kernel(int R, const int* __restrict__ counts,
+                                                                 int* __restrict__ sums) {
+  __shared__ int part[kScanThreads];
+  const int base = blockIdx.x * kScanChunk + threadIdx.x * kScanPer;
+  int s = 0;
+  for (int i = 0; i < kScanPer; ++i)
+    if (base + i < R) s += counts[base + i];
+  const int ex = block_exclusive_scan(s, part);
+  if (threadIdx.x == kScanThreads - 1) sums[blockIdx.x] = ex + s;
+}
+
+__global__ __launch_bounds__(1024) void chunk_offsets_kernel(int nc, int* __restrict__ sums) {
+  // exclusive scan of the nc chunk sums in place
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (nc + 1023) / 1024;
+  const int lo = min(nc, tid * per), hi = min(nc, lo + per);
+  int s = 0;
+  for (int c = lo; c < hi; ++c) s += sums[c];
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
   int run = part[tid] - s;
-  if (tid == 0) row_ptr[0] = 0;
-  for (int r = lo; r < hi; ++r) {
-    run += counts[r];
-    row_ptr[r + 1] = run;
+  for (int c = lo; c < hi; ++c) {
+    const int v = sums[c];
+    sums[c] = run;
+    run += v;
   }
 }
+
+__global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(int R, const int* __restrict__ counts,
+                                                                  const int* __restrict__ offsets,
+                                                                  int* __restrict__ row_ptr) {
+  __shared__ int part[kScanThreads];
+  const int base = blockIdx.x * kScanChunk + threadIdx.x * kScanPer;
+  int c[kScanPer];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    c[i] = base + i < R ? counts[base + i] : 0;
+    s += c[i];
+  }
+  int run = offsets[blockIdx.x] + block_exclusive_scan(s, part);
+  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    run += c[i];
+    if (base + i < R) row_ptr[base + i + 1] = run;
+  }
+}
+
+__global__ void zero_row_ptr_kernel(int* __restrict__ row_ptr) { row_ptr[0] = 0; }
 
 __global__ __launch_bounds__(256) void compact_kernel(Geom g, const int* __restrict__ row_ptr,
                                                       const uint32_t* __restrict__ mask, int mask_words,
@@ -411,11 +589,11 @@ hipError_t launch_scheme_choose(int BH, int C, const double* agg64, int* scheme,
 hipError_t launch_scores(const Geom& g, const float* q_mean, const float* k_mean, double scale,
                          double* scores, hipStream_t s) {
   if (g.BH == 0) return hipSuccess;
-  dim3 grid((g.nblk + kSRows - 1) / kSRows, (g.nblk + kSCols - 1) / kSCols, g.BH);
+  dim3 grid((g.nblk + kFRows - 1) / kFRows, g.BH);
   if (g.d == 128)
-    scores_kernel<128><<<grid, 256, 0, s>>>(g, q_mean, k_mean, scale, scores);
+    scores_kernel<128><<<grid, 64 * kFWaves, 0, s>>>(g, q_mean, k_mean, scale, scores);
   else
-    scores_kernel<64><<<grid, 256, 0, s>>>(g, q_mean, k_mean, scale, scores);
+    scores_kernel<64><<<grid, 64 * kFWaves, 0, s>>>(g, q_mean, k_mean, scale, scores);
   return hipGetLastError();
 }
 
@@ -423,19 +601,55 @@ hipError_t launch_select(const Geom& g, const double* scores, const SelectArgs& 
                          uint32_t* mask, int mask_words, hipStream_t s) {
   if (g.R == 0) return hipSuccess;
   const int grid = (g.R + 3) / 4;
-  if (g.nblk <= 64 * 4)
-    select_kernel<4><<<grid, 256, 0, s>>>(g, scores, a, counts, mask, mask_words);
-  else if (g.nblk <= 64 * 16)
-    select_kernel<16><<<grid, 256, 0, s>>>(g, scores, a, counts, mask, mask_words);
-  else if (g.nblk <= 64 * 32)
-    select_kernel<32><<<grid, 256, 0, s>>>(g, scores, a, counts, mask, mask_words);
-  else
-    select_kernel<64><<<grid, 256, 0, s>>>(g, scores, a, counts, mask, mask_words);
+  const int e = (g.nblk + 63) / 64;  // scores per lane
+#define SPADE_SELECT(EE) select_kernel<EE><<<grid, 256, 0, s>>>(g, scores, a, counts, mask, mask_words)
+  if (e <= 4) SPADE_SELECT(4);
+  else if (e <= 16) SPADE_SELECT(16);
+  else if (e <= 24) SPADE_SELECT(24);
+  else if (e <= 32) SPADE_SELECT(32);
+  else if (e <= 48) SPADE_SELECT(48);
+  else SPADE_SELECT(64);
+#undef SPADE_SELECT
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const Geom& g, const int* counts, int* row_ptr, hipStream_t s) {
-  scan_kernel<<<1, kScanThreads, 0, s>>>(g.R, counts, row_ptr);
+bool fused_select_fits(const Geom& g) { return g.nblk <= kFusedMaxBlocks; }
+
+hipError_t launch_estimate_select(const Geom& g, const float* q_mean, const float* k_mean, double scale,
+                                  const SelectArgs& a, int* counts, uint32_t* mask, int mask_words,
+                                  hipStream_t s) {
+  if (g.R == 0) return hipSuccess;
+  dim3 grid((g.nblk + kFRows - 1) / kFRows, g.BH);
+  const int e = (g.nblk + 63) / 64;  // scores per lane: the tile's width in units of 64
+#define SPADE_FUSED(EE)                                                                                         \
+  do {                                                                                                          \
+    if (g.d == 128)                                                                                             \
+      estimate_select_kernel<128, EE><<<grid, 64 * kFWaves, 0, s>>>(g, q_mean, k_mean, scale, a, counts, mask,  \
+                                                                    mask_words);                               \
+    else                                                                                                        \
+      estimate_select_kernel<64, EE><<<grid, 64 * kFWaves, 0, s>>>(g, q_mean, k_mean, scale, a, counts, mask,   \
+                                                                   mask_words);                                \
+  } while (0)
+  if (e <= 2) SPADE_FUSED(2);
+  else if (e <= 4) SPADE_FUSED(4);
+  else if (e <= 6) SPADE_FUSED(6);
+  else if (e <= 8) SPADE_FUSED(8);
+  else if (e <= 10) SPADE_FUSED(10);
+  else if (e <= 12) SPADE_FUSED(12);
+  else SPADE_FUSED(16);
+#undef SPADE_FUSED
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const Geom& g, const int* counts, int* row_ptr, int* chunk_sums, hipStream_t s) {
+  if (g.R == 0) {
+    zero_row_ptr_kernel<<<1, 1, 0, s>>>(row_ptr);
+    return hipGetLastError();
+  }
+  const int nc = scan_chunks(g.R);
+  chunk_sum_kernel<<<nc, kScanThreads, 0, s>>>(g.R, counts, chunk_sums);
+  chunk_offsets_kernel<<<1, 1024, 0, s>>>(nc, chunk_sums);
+  scan_apply_kernel<<<nc, kScanThreads, 0, s>>>(g.R, counts, chunk_sums, row_ptr);
   return hipGetLastError();
 }
 

@@ -78,7 +78,8 @@ struct SelectArgs {
 struct Workspace {
   size_t counts;    // int32 [R]
   size_t mask;      // uint32 [R * mask_words]
-  size_t scores;    // double [R * nblk]
+  size_t scores;    // double [R * nblk] (only when the fused select does not fit)
+  size_t scan;      // int32 [scan_chunks(R) + 1]: chunk sums of the CSR scan
   size_t qmean;     // float [BH * nblk * d]
   size_t kmean;     // float [BH * nblk * d]
   size_t qpack;     // bf16 [BH * nblk * P * d]
@@ -108,7 +109,17 @@ hipError_t launch_scores(const Geom& g, const float* q_mean, const float* k_mean
                          double* scores, hipStream_t s);
 hipError_t launch_select(const Geom& g, const double* scores, const SelectArgs& a, int* counts,
                          uint32_t* mask, int mask_words, hipStream_t s);
-hipError_t launch_scan(const Geom& g, const int* counts, int* row_ptr, hipStream_t s);
+// Estimator and index search in one kernel, the scores of a 16-row tile kept
+// in LDS (never written to HBM); for nblk <= kFusedMaxBlocks.
+constexpr int kFusedMaxBlocks = 1024;
+bool fused_select_fits(const Geom& g);
+hipError_t launch_estimate_select(const Geom& g, const float* q_mean, const float* k_mean, double scale,
+                                  const SelectArgs& a, int* counts, uint32_t* mask, int mask_words,
+                                  hipStream_t s);
+// row_ptr from the counts; chunk_sums holds scan_chunks(R) ints (unused when R == 0)
+constexpr int kScanChunk = 4096;
+inline int scan_chunks(long long R) { return (int)((R + kScanChunk - 1) / kScanChunk); }
+hipError_t launch_scan(const Geom& g, const int* counts, int* row_ptr, int* chunk_sums, hipStream_t s);
 hipError_t launch_compact(const Geom& g, const int* row_ptr, const uint32_t* mask, int mask_words,
                           int* col_idx, hipStream_t s);
 hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpack, const void* vpack,

@@ -11,6 +11,7 @@ Bars (block-sparse attention contract):
 * outputs, computed with the GPU's CSR fed to the oracle: max-abs error
   <= 2e-2 for bf16 and <= 1e-5 for the fp32 debug path.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -329,12 +330,15 @@ def test_per_head_budgets_match_oracle(name, mode, budget):
 # the supported limits: 4096 and 1728 blocks per head (the widest selection
 # rows), and 1024-token blocks (eight 128-query tiles per row, 32 key subtiles
 # per block)
-LIMITS = ["max_blocks", "blocks_2k", "max_block_tokens"]
+LIMITS = ["max_blocks", "blocks_2k", "max_block_tokens", "max_blocks_mass"]
 
 
 @pytest.mark.parametrize("name", LIMITS)
 def test_limits_selection_and_attention_match_oracle(name):
-    cfg = synth.get_config(name)
+    # max_blocks_mass: 4096 blocks under a mass budget (the widest rows of the
+    # mass search, 64 scores per lane)
+    cfg = (synth.get_config("max_blocks").with_budget("mass", 0.5) if name == "max_blocks_mass"
+           else synth.get_config(name))
     print(f"[limits] {name}", flush=True)
     x = synth.make_inputs(cfg)
     g = geom(cfg)
@@ -487,9 +491,59 @@ def test_deterministic_and_writes_every_output_once():
 FULL = [("small", None), ("mid", None), ("large", None), ("ragged", 1.0), ("ragged", 0.5), ("ragged", 0.1)]
 
 
+def parity_rows(cfg, nblk, seed):
+    """Every row of the first and the last (batch, head) pair plus 256 seeded
+    rows of the whole layer, ascending."""
+    BH = cfg.B * cfg.H
+    R = BH * nblk
+    rows = set(range(nblk)) | set(range((BH - 1) * nblk, BH * nblk))
+    rng = np.random.default_rng(seed)
+    rows |= set(rng.choice(R, size=min(R, 256), replace=False).tolist())
+    return sorted(rows)
+
+
+def bf16_half_ulp(x):
+    """Half a bf16 ulp at |x| (8 significant bits)."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 8)
+
+
+def check_rows(cfg, x, o, rp, ci, rows, tol, label):
+    """Oracle attention of the given rows on the GPU's CSR against the GPU
+    output; returns (max-abs error, max |o|, the error in half-ulps of a bf16
+    value of that largest magnitude: about 1 means the output's own rounding
+    dominates)."""
+    g = geom(cfg)
+    scale = oracle.default_scale(cfg.d)
+    toks = oracle.block_tokens(g)
+    of = o.cpu()
+    worst = omax = 0.0
+    cur = None
+    for r in rows:
+        bh, i = divmod(r, g.nblk)
+        if bh != cur:
+            b, h = divmod(bh, cfg.H)
+            qh, kh, vh = (to_f64(cfg, x[n][b, h]) for n in ("q", "k", "v"))
+            got_h = of[b, h].float().numpy().astype(np.float64)
+            cur = bh
+        ref = oracle.attention_block_row(qh, kh, vh, toks, i, ci[rp[r]:rp[r + 1]].tolist(), scale)
+        err = np.abs(got_h[toks[i]] - ref)
+        worst = max(worst, float(err.max()))
+        omax = max(omax, float(np.abs(ref).max()))
+    ulps = worst / float(bf16_half_ulp(omax))
+    print(f"[full] {label}: {len(rows)} rows, max-abs {worst:.3e}, max |o| {omax:.3f}, "
+          f"error {ulps:.2f} bf16 half-ulps at max |o|", flush=True)
+    assert worst <= tol, (label, worst)
+    return worst, omax, ulps
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name,ratio", FULL)
 def test_full_size_selection_and_sampled_rows(name, ratio):
+    """The bench's launch configuration at full size: every row's block set
+    against the oracle, and every output element of all rows of the first and
+    the last head plus 256 seeded rows (queue stealing, unions of hundreds of
+    blocks and the all-head launch only happen at this size)."""
     cfg = synth.get_config(name)
     if ratio is not None:
         cfg = cfg.with_budget("ratio", ratio)
@@ -504,21 +558,7 @@ def test_full_size_selection_and_sampled_rows(name, ratio):
     ndiff = compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), cfg.name)
     print(f"[full] {cfg.name}: rows {len(sel.counts)}, differing {ndiff}, "
           f"ambiguous(m<=1e-3) {(sel.margins <= 1e-3).sum()}", flush=True)
-    R = len(sel.counts)
-    rng = np.random.default_rng(cfg.seed)
-    rows = sorted(set([0, R - 1] + rng.choice(R, size=6, replace=False).tolist()))
-    of = o.cpu()
-    toks = oracle.block_tokens(g)
-    worst = 0.0
-    for r in rows:
-        bh, i = divmod(r, g.nblk)
-        b, h = divmod(bh, cfg.H)
-        qh, kh, vh = (to_f64(cfg, x[n][b, h]) for n in ("q", "k", "v"))
-        ref = oracle.attention_block_row(qh, kh, vh, toks, i, ci[rp[r]:rp[r + 1]].tolist(), scale)
-        got = of[b, h, toks[i]].float().numpy().astype(np.float64)
-        worst = max(worst, np.abs(got - ref).max())
-    print(f"[full] {cfg.name}: sampled rows {rows} max-abs {worst:.3e}", flush=True)
-    assert worst <= BF16_TOL
+    check_rows(cfg, x, o, rp, ci, parity_rows(cfg, g.nblk, cfg.seed), BF16_TOL, cfg.name)
 
 
 @pytest.mark.slow
@@ -651,6 +691,73 @@ def test_attn_schemes_with_window_and_summarizer(name, window, summarizer):
     assert (same | (margin <= 1e-9)).all()
     tol = BF16_TOL if cfg.dtype == "bf16" else F32_TOL
     assert np.abs(dev_to_f64(o)[same] - ref[same]).max() <= tol
+
+
+@pytest.mark.slow
+def test_full_size_attn_schemes_ragged():
+    """Head-wise schemes at full size (the Ragged layer at ratio 0.5, where
+    two of the three candidates win): every head equals its single-scheme run
+    bit for bit, and each single-scheme run matches the oracle on all rows of
+    the first and last head that chose it plus sampled rows, with its CSR."""
+    cfg = synth.get_config("ragged").with_budget("ratio", 0.5)
+    print(f"[full schemes attn] {cfg.name}", flush=True)
+    x = synth.make_inputs(cfg)
+    cands = candidates_for(cfg)
+    grid = (cfg.T, cfg.Hh, cfg.W)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    o, scheme, agg = spade.attn_schemes(q, k, v, grid, cands, cfg.mode, cfg.per_head_budget())
+    torch.cuda.synchronize()
+    sch = scheme.cpu().numpy()
+    counts = np.bincount(sch.ravel(), minlength=len(cands))
+    print(f"[full schemes attn] choices {counts}", flush=True)
+    assert (counts > 0).sum() >= 2  # head grouping really splits the launch
+    ref = oracle.scheme_aggregate(to_f64(cfg, x["q"]), to_f64(cfg, x["k"]), cfg.T, cfg.Hh, cfg.W, cands)
+    choice, margin = oracle.choose_scheme(ref)
+    assert ((sch == choice) | (margin <= 1e-9)).all()
+    for c, blk in enumerate(cands):
+        m = sch == c
+        if not m.any():
+            continue
+        oc, rp, ci = spade.attn(q, k, v, grid, blk, cfg.mode, cfg.per_head_budget())
+        assert torch.equal(o[torch.from_numpy(m).cuda()], oc[torch.from_numpy(m).cuda()]), c
+        cc = dataclasses.replace(cfg, bt=blk[0], bh=blk[1], bw=blk[2])
+        g = geom(cc)
+        heads = [b * cfg.H + h for b in range(cfg.B) for h in range(cfg.H) if m[b, h]]
+        rows = set(range(heads[0] * g.nblk, (heads[0] + 1) * g.nblk))
+        rows |= set(range(heads[-1] * g.nblk, (heads[-1] + 1) * g.nblk))
+        rng = np.random.default_rng(cfg.seed + c)
+        for bh in rng.choice(heads, size=min(len(heads), 8), replace=False).tolist():
+            rows |= set((bh * g.nblk + rng.choice(g.nblk, size=16, replace=False)).tolist())
+        rp_h, ci_h = csr_rows(rp, ci)
+        check_rows(cc, x, oc, rp_h, ci_h, sorted(rows), BF16_TOL, f"{cfg.name} candidate {blk}")
+
+
+def test_f32_debug_path_with_large_logits():
+    """The fp32 debug path on the mid block shape with hot blocks (+3 on every
+    channel of some blocks): logits reach about 110, where fp32 rounding of
+    the 128-term dot products alone moves a logit by about sqrt(d) 2^-24 |logit|.
+    Selection must match the oracle; the output error is held to that
+    arithmetic's bound 8 sqrt(d) 2^-24 L max|v| (L the largest scale |q| |k|
+    of the layer) and reported, next to the 1e-5 bar of small logits."""
+    base = synth.get_config("mid_shape")
+    cfg = dataclasses.replace(base, name="mid_shape_f32", dtype="f32")
+    x = synth.make_inputs(cfg)
+    g = geom(cfg)
+    o, rp, ci = run_attn(cfg, x)
+    rp, ci = csr_rows(rp, ci)
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    scale = oracle.default_scale(cfg.d)
+    S_ref = oracle.estimate(oracle_means(cfg, x["q"]), oracle_means(cfg, x["k"]), scale)
+    sel = oracle.select(S_ref, cfg.mode, cfg.per_head_budget())
+    assert compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), cfg.name) == 0
+    ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], g, rp, ci, scale)
+    err = float(np.abs(dev_to_f64(o) - ref).max())
+    nq = np.linalg.norm(xf["q"], axis=-1).max()
+    nk = np.linalg.norm(xf["k"], axis=-1).max()
+    L = scale * nq * nk
+    bound = 8 * math.sqrt(cfg.d) * 2.0 ** -24 * L * np.abs(xf["v"]).max()
+    print(f"[f32 large logits] max logit bound {L:.1f}, max-abs error {err:.3e}, bound {bound:.3e}", flush=True)
+    assert err <= max(F32_TOL, bound)
 
 
 def test_single_candidate_equals_the_plain_path():
