@@ -26,8 +26,10 @@
  *   workspace are DEVICE pointers owned by the caller.  spade_problem and
  *   spade_budget (and budget->per_head) are HOST memory read during the call.
  *   The library never allocates or frees device memory.  Its only state is
- *   a per-device cache of the compute-unit count and the per-thread events of
- *   spade_profile_events.
+ *   a per-device cache of the compute-unit count, the per-thread events of
+ *   spade_profile_events and, on each device it runs on, one static device
+ *   buffer of SPADE_STATIC_SCRATCH_BYTES (part of the loaded code object,
+ *   held until the process ends) that spade_estimate_select_static uses.
  * - The workspace holds per-call scratch (summaries, scores, packed operand
  *   tiles, the attention kernel's unit counter): calls that may run at the same time,
  *   on one stream or several, each need a workspace of their own.
@@ -168,6 +170,32 @@ spade_status spade_summarize_sics(const spade_problem* p, const void* q, const v
 spade_status spade_estimate_select(const spade_problem* p, const float* q_mean, const float* k_mean,
                                    const spade_budget* budget, int32_t* row_ptr, int32_t* col_idx,
                                    int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream);
+
+/* Size of the library's static selection buffer, per device. */
+#define SPADE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* spade_estimate_select for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same results, with the selection
+ * scratch (per-row counts, row bitmasks, scan chunk sums) in the library's
+ * static device buffer instead of a workspace.  That scratch is
+ *   align256(4 R) + align256(4 R ceil(nblk/32)) + align256(4 (ceil(R/4096) + 1))
+ * bytes for nblk <= 1024 (wider rows would add 8 R nblk bytes of fp64 scores,
+ * more than the buffer holds).  A problem whose scratch exceeds
+ * SPADE_STATIC_SCRATCH_BYTES is rejected with SPADE_ERR_CAPACITY before
+ * anything is launched (about 99k rows of 630 blocks fit; a 40-head layer of
+ * 630 blocks needs 2.02 MiB).  The call makes no
+ * device allocation of any kind.  On first use on a device it looks up that
+ * device's buffer address (so call it with the stream's device current).
+ * Every call on one device shares its buffer, which keeps the last call's
+ * contents (no call relies on them).  Calls that may run at the same time on
+ * one device (on several streams, or graphs replayed concurrently) race on
+ * it: serialize them, for example on one stream.
+ * Other arguments and errors as spade_estimate_select. */
+spade_status spade_estimate_select_static(const spade_problem* p, const float* q_mean,
+                                          const float* k_mean, const spade_budget* budget,
+                                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                          void* stream);
 
 /* Flash block-sparse attention ("Flash Block-Sparse Attention"): for every
  * query token of Q block i, softmax(scale * q K_sel^T) V_sel over all tokens of

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     SPADE_KEEP_COUNT, SPADE_KEEP_MASS, SPADE_KEEP_RATIO, SPADE_OK, SPADE_ERR_CAPACITY,
     SPADE_ERR_DEVICE, SPADE_ERR_INVALID_ARG, SPADE_ERR_UNSUPPORTED, lib, spade_attn,
     spade_block_sparse_attn, spade_check, spade_debug_scores, spade_estimate_select,
+    spade_estimate_select_static, SPADE_STATIC_SCRATCH_BYTES,
     spade_attn_schemes, spade_max_nnz, spade_num_blocks, spade_profile_events, spade_scheme_select,
     spade_schemes_workspace_bytes, spade_summarize, spade_summarize_sics,
     spade_workspace_bytes,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "Problem", "Budget", "SpadeError", "problem_for", "summarize", "summarize_sics", "estimate_select",
+    "estimate_select_static", "spade_estimate_select_static", "SPADE_STATIC_SCRATCH_BYTES",
     "block_sparse_attn", "attn", "debug_scores", "alloc_workspace", "scheme_select", "attn_schemes",
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
     "spade_summarize", "spade_summarize_sics", "spade_estimate_select", "spade_block_sparse_attn", "spade_attn",
@@ -160,6 +162,33 @@ def estimate_select(q_mean, k_mean, problem: Problem, mode, per_head: Sequence[f
     row_ptr = torch.empty(R + 1, dtype=torch.int32, device=q_mean.device)
     col_idx = torch.empty(max(1, cap), dtype=torch.int32, device=q_mean.device)
     spade_estimate_select(problem, q_mean, k_mean, bud, row_ptr, col_idx, cap, ws, ws.numel())
+    return row_ptr, col_idx
+
+
+def estimate_select_static(q_mean, k_mean, problem: Problem, mode, per_head: Sequence[float], window=None,
+                           out=None):
+    """estimate_select with the library's static scratch instead of a
+    workspace: the C call allocates nothing.  out=(row_ptr, col_idx) reuses
+    caller buffers (row_ptr int32 [R+1], col_idx int32 with at least
+    spade_max_nnz entries); otherwise they are allocated here."""
+    torch = _torch()
+    shape = _summary_shape(problem)
+    specs = [(q_mean, "q_mean", shape, torch.float32), (k_mean, "k_mean", shape, torch.float32)]
+    bud = Budget(mode, per_head, window)
+    cap = spade_max_nnz(problem, bud)
+    if cap < 0:
+        raise SpadeError(spade_check(problem, bud), "estimate_select_static")
+    R = problem.B * problem.H * shape[2]
+    if out is None:
+        row_ptr = torch.empty(R + 1, dtype=torch.int32, device=q_mean.device)
+        col_idx = torch.empty(max(1, cap), dtype=torch.int32, device=q_mean.device)
+    else:
+        row_ptr, col_idx = out
+        specs += [(row_ptr, "row_ptr", (R + 1,), torch.int32), (col_idx, "col_idx", None, torch.int32)]
+    _check_tensors(specs)
+    if col_idx.dim() != 1:
+        raise SpadeError(SPADE_ERR_INVALID_ARG, "col_idx must be 1-D")
+    spade_estimate_select_static(problem, q_mean, k_mean, bud, row_ptr, col_idx, col_idx.numel())
     return row_ptr, col_idx
 
 

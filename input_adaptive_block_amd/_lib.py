@@ -23,6 +23,8 @@ SPADE_ERR_UNSUPPORTED = 2
 SPADE_ERR_CAPACITY = 3
 SPADE_ERR_DEVICE = 4
 
+SPADE_STATIC_SCRATCH_BYTES = 8 << 20  # the header's static selection buffer, per device
+
 SPADE_BF16 = 0
 SPADE_F32 = 1
 
@@ -133,6 +135,7 @@ def _load() -> ctypes.CDLL:
         "spade_summarize": (st, [P, vp, vp, vp, vp, vp]),
         "spade_summarize_sics": (st, [P, vp, vp, vp, vp, vp, vp, vp]),
         "spade_estimate_select": (st, [P, vp, vp, Bp, vp, vp, i64, vp, sz, vp]),
+        "spade_estimate_select_static": (st, [P, vp, vp, Bp, vp, vp, i64, vp]),
         "spade_block_sparse_attn": (st, [P, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
         "spade_attn": (st, [P, vp, vp, vp, Bp, vp, vp, vp, i64, vp, sz, vp]),
         "spade_debug_scores": (st, [P, vp, vp, vp, vp]),
@@ -153,6 +156,7 @@ _LIB = _load()
 EXPORTED = (
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
     "spade_status_string", "spade_summarize", "spade_summarize_sics", "spade_estimate_select",
+    "spade_estimate_select_static",
     "spade_block_sparse_attn", "spade_attn", "spade_debug_scores",
     "spade_profile_events",
     "spade_schemes_workspace_bytes", "spade_scheme_select", "spade_attn_schemes",
@@ -226,6 +230,14 @@ def spade_estimate_select(problem: Problem, q_mean, k_mean, budget: Budget, row_
                                       ctypes.byref(budget.c()), _ptr(row_ptr), _ptr(col_idx),
                                       int(col_capacity), _ptr(workspace), int(ws_bytes), _stream(stream)),
            "spade_estimate_select")
+
+
+def spade_estimate_select_static(problem: Problem, q_mean, k_mean, budget: Budget, row_ptr, col_idx,
+                                 col_capacity: int, stream=None) -> None:
+    _check(_LIB.spade_estimate_select_static(ctypes.byref(problem.c()), _ptr(q_mean), _ptr(k_mean),
+                                             ctypes.byref(budget.c()), _ptr(row_ptr), _ptr(col_idx),
+                                             int(col_capacity), _stream(stream)),
+           "spade_estimate_select_static")
 
 
 def spade_block_sparse_attn(problem: Problem, q, k, v, row_ptr, col_idx, col_capacity: int, o,

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspade.so")
-SOURCES = ["api.cpp", "summarize.hip", "select.hip", "bsattn.hip"]
+SOURCES = ["api.cpp", "summarize.hip", "select.hip", "bsattn.hip", "static_scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -209,6 +209,7 @@ Workspace workspace_layout(const Geom& g) {
   // fp64 scores in HBM only for rows wider than the fused kernel's LDS tile
   L.scores = off; off = align256(off + (fused_select_fits(g) ? 0 : (size_t)g.R * g.nblk * 8));
   L.scan = off; off = align256(off + ((size_t)scan_chunks(g.R) + 1) * 4);
+  L.select_total = off;  // everything above is all that selection touches
   L.qmean = off; off = align256(off + (size_t)g.BH * g.nblk * g.d * 4);
   L.kmean = off; off = align256(off + (size_t)g.BH * g.nblk * g.d * 4);
   // packed tiles plus two spare 32-row subtiles: the attention kernel copies
@@ -220,6 +221,28 @@ Workspace workspace_layout(const Geom& g) {
   L.counter = off; off = align256(off + 4);
   L.total = off;
   return L;
+}
+
+spade_status estimate_select_entry(const spade_problem* p, const float* q_mean, const float* k_mean,
+                                   const spade_budget* budget, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, void* ws, size_t ws_bytes, ScratchLookup lookup,
+                                   hipStream_t s) {
+  Geom g;
+  SPADE_TRY(make_geom(p, &g));
+  SPADE_TRY(check_budget(budget, g));
+  const long long need = max_nnz(g, budget);
+  if (need >= (1LL << 31)) return SPADE_ERR_UNSUPPORTED;
+  if (col_capacity < need) return SPADE_ERR_CAPACITY;
+  if (!row_ptr) return SPADE_ERR_INVALID_ARG;
+  const Workspace L = workspace_layout(g);
+  // a caller's workspace is checked against the documented whole size; the
+  // library's own buffer only has to hold the selection part
+  if (ws_bytes < (lookup ? L.select_total : L.total)) return SPADE_ERR_CAPACITY;
+  if (g.R == 0) return dev(launch_scan(g, nullptr, row_ptr, nullptr, s));
+  if (!q_mean || !k_mean || !col_idx) return SPADE_ERR_INVALID_ARG;
+  if (lookup) SPADE_TRY(dev(lookup(&ws)));
+  if (!ws) return SPADE_ERR_INVALID_ARG;
+  return run_select(p, g, L, q_mean, k_mean, budget, row_ptr, col_idx, ws, s);
 }
 
 }  // namespace spade
@@ -293,19 +316,8 @@ spade_status spade_summarize_sics(const spade_problem* p, const void* q, const v
 spade_status spade_estimate_select(const spade_problem* p, const float* q_mean, const float* k_mean,
                                    const spade_budget* budget, int32_t* row_ptr, int32_t* col_idx,
                                    int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream) {
-  Geom g;
-  SPADE_TRY(make_geom(p, &g));
-  SPADE_TRY(check_budget(budget, g));
-  const long long need = max_nnz(g, budget);
-  if (need >= (1LL << 31)) return SPADE_ERR_UNSUPPORTED;
-  if (col_capacity < need) return SPADE_ERR_CAPACITY;
-  if (!row_ptr) return SPADE_ERR_INVALID_ARG;
-  const Workspace L = workspace_layout(g);
-  if (ws_bytes < L.total) return SPADE_ERR_CAPACITY;
-  hipStream_t s = (hipStream_t)stream;
-  if (g.R == 0) return dev(launch_scan(g, nullptr, row_ptr, nullptr, s));
-  if (!q_mean || !k_mean || !col_idx || !workspace) return SPADE_ERR_INVALID_ARG;
-  return run_select(p, g, L, q_mean, k_mean, budget, row_ptr, col_idx, workspace, s);
+  return estimate_select_entry(p, q_mean, k_mean, budget, row_ptr, col_idx, col_capacity, workspace, ws_bytes,
+                               nullptr, (hipStream_t)stream);
 }
 
 spade_status spade_block_sparse_attn(const spade_problem* p, const void* q, const void* k, const void* v,

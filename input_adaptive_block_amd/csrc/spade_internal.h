@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/spade.h"
+
 namespace spade {
 
 constexpr int kMaxHeads = 256;     // per-head budgets travel as kernel arguments
@@ -80,6 +82,7 @@ struct Workspace {
   size_t mask;      // uint32 [R * mask_words]
   size_t scores;    // double [R * nblk] (only when the fused select does not fit)
   size_t scan;      // int32 [scan_chunks(R) + 1]: chunk sums of the CSR scan
+  size_t select_total;  // bytes of the four regions above: all that selection touches
   size_t qmean;     // float [BH * nblk * d]
   size_t kmean;     // float [BH * nblk * d]
   size_t qpack;     // bf16 [BH * nblk * P * d]
@@ -128,5 +131,21 @@ hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpac
 hipError_t launch_bsattn_f32(const Geom& g, const float* q, const float* k, const float* v,
                              const int* row_ptr, const int* col_idx, long long col_capacity,
                              float scale, float* o, hipStream_t s);
+
+// ---- entry-point bodies shared between source files ----------------------
+
+// Returns the device address of a library-owned scratch buffer for the
+// current device.
+typedef hipError_t (*ScratchLookup)(void** ptr);
+
+// Checks and launches of the estimate + select entry point.  Without lookup,
+// ws is the caller's workspace and ws_bytes must cover the whole documented
+// workspace; with lookup, ws_bytes is the library buffer's size, checked
+// against the selection part only, and lookup supplies ws after every
+// argument check has passed (so rejected calls touch no device).
+spade_status estimate_select_entry(const spade_problem* p, const float* q_mean, const float* k_mean,
+                                   const spade_budget* budget, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, void* ws, size_t ws_bytes, ScratchLookup lookup,
+                                   hipStream_t s);
 
 }  // namespace spade

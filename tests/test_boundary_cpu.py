@@ -284,3 +284,50 @@ def test_attn_checks_workspace():
             workspace=torch.zeros(2, need, dtype=torch.uint8))
     _raises("q must be a device tensor", INVALID, spade.attn, q, q, q, grid, block, "count", [3] * cfg.H,
             workspace=torch.zeros(need, dtype=torch.uint8))
+
+
+def _static_scratch_need(p, nblk):
+    """The selection scratch of spade_estimate_select_static, as the header
+    states it."""
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    R = p.B * p.H * nblk
+    wide = 8 * R * nblk if nblk > 1024 else 0
+    return a(4 * R) + a(4 * R * ((nblk + 31) // 32)) + a(wide) + a(4 * ((R + 4095) // 4096 + 1))
+
+
+def test_static_select_rejects_before_device():
+    """The allocation-free entry point checks its arguments, and the size of
+    the static buffer, before it looks up that buffer or launches anything."""
+    text = open(os.path.join(ROOT, "include", "spade.h")).read()
+    m = re.search(r"#define SPADE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == spade.SPADE_STATIC_SCRATCH_BYTES
+    cfg = synth.get_config("mid")
+    p = _prob(cfg)
+    b = spade.Budget("mass", [0.9] * cfg.H)
+    cap = spade.spade_max_nnz(p, b)
+    for args, status in [((0, 0, b, 1, 1, cap - 1), CAP), ((0, 0, b, 0, 1, cap), INVALID),
+                         ((0, 0, b, 1, 1, cap), INVALID)]:
+        with pytest.raises(spade.SpadeError) as e:
+            spade.spade_estimate_select_static(p, *args, stream=0)
+        assert e.value.status == status, args
+    assert _static_scratch_need(p, 630) == 2016000 + 100864 + 256  # 2.02 MiB for the 40-head layer
+    # batches of that layer: accepted (then stopped by the null summaries) up
+    # to the buffer's size, CAPACITY beyond it
+    seen = set()
+    for B in range(1, 7):
+        q = _prob(cfg, B=B)
+        fits = _static_scratch_need(q, 630) <= spade.SPADE_STATIC_SCRATCH_BYTES
+        seen.add(fits)
+        with pytest.raises(spade.SpadeError) as e:
+            spade.spade_estimate_select_static(q, 0, 0, b, 1, 1, spade.spade_max_nnz(q, b), stream=0)
+        assert e.value.status == (INVALID if fits else CAP), B
+    assert seen == {True, False}
+    # rows wider than 1024 blocks would keep their fp64 scores there too,
+    # more than the buffer holds even for one head
+    q = spade.Problem(1, 1, 32 * 33, 64, 1, 32, 33, 1, 1, 1, spade.SPADE_BF16, 0.0)
+    nblk = spade.spade_num_blocks(q)
+    assert nblk == 1056 and _static_scratch_need(q, nblk) > spade.SPADE_STATIC_SCRATCH_BYTES
+    bw = spade.Budget("ratio", [0.1])
+    with pytest.raises(spade.SpadeError) as e:
+        spade.spade_estimate_select_static(q, 0, 0, bw, 1, 1, spade.spade_max_nnz(q, bw), stream=0)
+    assert e.value.status == CAP
