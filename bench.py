@@ -265,6 +265,15 @@ def main():
     sagg = torch.empty(len(cands), cfg.B * cfg.H, dtype=torch.float32, device=dev)
     ssch = torch.empty(cfg.B * cfg.H, dtype=torch.int32, device=dev)
     scheme_ms = timed(lambda: spade.spade_scheme_select(p, q, k, cands, sagg, ssch, sws, sws_n, stream))
+    # the head-wise path end to end over the same candidates (choice, then one
+    # segment of summarize + select + attention per candidate)
+    aws_n = spade.spade_schemes_workspace_bytes(p, cands, bud)
+    aws = torch.empty(aws_n, dtype=torch.uint8, device=dev)
+    schemes_ms = timed(lambda: spade.spade_attn_schemes(p, q, k, v, cands, bud, o2, sagg, ssch, aws, aws_n,
+                                                        stream), reps=3)
+    torch.cuda.synchronize()
+    choice = np.bincount(ssch.cpu().numpy(), minlength=len(cands)).tolist()
+    del aws
     sel_ms = timed(lambda: spade.spade_estimate_select(p, qm, km, bud, rp2, ci2, cap, ws, ws.numel(), stream))
     bsa_ms = timed(lambda: spade.spade_block_sparse_attn(p, q, k, v, rp, ci, cap, o2, ws, ws.numel(), stream))
     summ_bytes = 2 * q.numel() * q.element_size() + 2 * qm.numel() * 4
@@ -301,6 +310,9 @@ def main():
             "summarize_with_sics": sics_ms,
             "summarize_with_sics_GBps": (summ_bytes + 2 * qs.numel() * 4) / (sics_ms * 1e-3) / 1e9,
             "scheme_select_3_candidates": scheme_ms,
+            "attn_schemes_3_candidates": schemes_ms,
+            "attn_schemes_heads_per_candidate": choice,
+            "attn_schemes_candidates": cands,
             "estimate_select": sel_ms,
             "block_sparse_attn_call": bsa_ms,
             "attention_kernel": attn_avg,

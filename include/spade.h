@@ -249,7 +249,13 @@ spade_status spade_scheme_select(const spade_problem* p, const void* q, const vo
  * sparse attention) over the heads that chose it (Head Grouping), each with
  * its own blocking; every output element is written by exactly one segment.
  * budget as for spade_attn, valid for every candidate's block count.  The
- * CSR of each segment stays in the workspace.  No host synchronisation. */
+ * CSR of each segment stays in the workspace.  No host synchronisation.
+ * For bf16, candidate 0's per-block SICS come from one fused pass over every
+ * head that also summarizes and packs Q, K, V into its operand tiles (gist.
+ * science technical summary, "Methodology 3", Kernel Fusion: blocking,
+ * summarization and intra-block estimation in one kernel); candidate 0's
+ * segment reuses those tiles.  agg and scheme equal spade_scheme_select's
+ * bit for bit. */
 spade_status spade_attn_schemes(const spade_problem* p, const void* q, const void* k, const void* v,
                                 const spade_block_shape* candidates, int32_t num_candidates,
                                 const spade_budget* budget, void* o, float* agg, int32_t* scheme,

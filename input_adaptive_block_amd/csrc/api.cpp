@@ -464,15 +464,27 @@ spade_status scheme_layout(const Geom* gs, int C, const spade_budget* budget, Sc
   return SPADE_OK;
 }
 
+// Aggregate SICS of every candidate and the head-wise choice.  With pipe set
+// (bf16 head-wise attention), candidate 0's SICS come from its pack pass over
+// every head -- layout transformation, summarization and intra-block
+// estimation in one read of Q, K, V -- whose tiles its launch segment reuses.
 spade_status run_scheme_select(const spade_problem* p, const Geom* gs, int C, const SchemeLayout& L,
-                               const void* q, const void* k, float* agg, int32_t* scheme, void* ws,
-                               hipStream_t s) {
+                               const void* q, const void* k, const void* v, void* pipe, float* agg,
+                               int32_t* scheme, void* ws, hipStream_t s) {
   double* agg64 = reinterpret_cast<double*>(ws_ptr(ws, L.agg64));
   float* qs = reinterpret_cast<float*>(ws_ptr(ws, L.qsics));
   float* ks = reinterpret_cast<float*>(ws_ptr(ws, L.ksics));
   const bool bf16 = p->dtype == SPADE_BF16;
   for (int c = 0; c < C; ++c) {
-    SPADE_TRY(dev(launch_summarize_sics(gs[c], bf16, q, k, nullptr, nullptr, qs, ks, s)));
+    if (c == 0 && pipe != nullptr && bf16) {
+      const Workspace W = workspace_layout(gs[0]);
+      SPADE_TRY(dev(launch_summarize_pack_sics(
+          gs[0], q, k, v, reinterpret_cast<float*>(ws_ptr(pipe, W.qmean)),
+          reinterpret_cast<float*>(ws_ptr(pipe, W.kmean)), ws_ptr(pipe, W.qpack), ws_ptr(pipe, W.kpack),
+          ws_ptr(pipe, W.vpack), qs, ks, s)));
+    } else {
+      SPADE_TRY(dev(launch_summarize_sics(gs[c], bf16, q, k, nullptr, nullptr, qs, ks, s)));
+    }
     SPADE_TRY(dev(launch_scheme_aggregate(gs[c], qs, ks, c, agg64, agg, s)));
   }
   return dev(launch_scheme_choose(gs[0].BH, C, agg64, scheme, s));
@@ -501,7 +513,8 @@ spade_status spade_scheme_select(const spade_problem* p, const void* q, const vo
   if (ws_bytes < L.total_select) return SPADE_ERR_CAPACITY;
   if (gs[0].BH == 0) return SPADE_OK;
   if (!q || !k || !scheme || !workspace) return SPADE_ERR_INVALID_ARG;
-  return run_scheme_select(p, gs, num_candidates, L, q, k, agg, scheme, workspace, (hipStream_t)stream);
+  return run_scheme_select(p, gs, num_candidates, L, q, k, nullptr, nullptr, agg, scheme, workspace,
+                           (hipStream_t)stream);
 }
 
 spade_status spade_attn_schemes(const spade_problem* p, const void* q, const void* k, const void* v,
@@ -517,11 +530,11 @@ spade_status spade_attn_schemes(const spade_problem* p, const void* q, const voi
   if (gs[0].BH == 0) return SPADE_OK;
   if (!q || !k || !v || !o || !scheme || !workspace) return SPADE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  SPADE_TRY(run_scheme_select(p, gs, num_candidates, L, q, k, agg, scheme, workspace, s));
+  void* pw = ws_ptr(workspace, L.pipe);
+  SPADE_TRY(run_scheme_select(p, gs, num_candidates, L, q, k, v, pw, agg, scheme, workspace, s));
   // one launch segment per candidate over the heads that chose it
   int32_t* row_ptr = reinterpret_cast<int32_t*>(ws_ptr(workspace, L.row_ptr));
   int32_t* col_idx = reinterpret_cast<int32_t*>(ws_ptr(workspace, L.col_idx));
-  void* pw = ws_ptr(workspace, L.pipe);
   const float scale = attn_scale(p);
   for (int c = 0; c < num_candidates; ++c) {
     Geom g = gs[c];
@@ -534,7 +547,8 @@ spade_status spade_attn_schemes(const spade_problem* p, const void* q, const voi
       void* qp = ws_ptr(pw, W.qpack);
       void* kp = ws_ptr(pw, W.kpack);
       void* vp = ws_ptr(pw, W.vpack);
-      SPADE_TRY(dev(launch_summarize(g, true, q, k, v, qm, km, qp, kp, vp, s)));
+      // candidate 0's tiles and means are already in place for every head
+      if (c > 0) SPADE_TRY(dev(launch_summarize(g, true, q, k, v, qm, km, qp, kp, vp, s)));
       SPADE_TRY(run_select(p, g, W, qm, km, budget, row_ptr, col_idx, pw, s));
       SPADE_TRY(dev(launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, L.cap, scale, o,
                                        reinterpret_cast<int*>(ws_ptr(pw, W.counter)), num_cus(), s)));

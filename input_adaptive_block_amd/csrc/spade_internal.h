@@ -103,6 +103,11 @@ hipError_t launch_summarize(const Geom& g, bool bf16, const void* q, const void*
 // pointer may be null)
 hipError_t launch_summarize_sics(const Geom& g, bool bf16, const void* q, const void* k, float* q_mean,
                                  float* k_mean, float* q_sics, float* k_sics, hipStream_t s);
+// bf16 only: the pack pass of launch_summarize (means + Q/K/V operand tiles)
+// that also writes the SICS of every Q and K block, in one read of Q, K, V
+hipError_t launch_summarize_pack_sics(const Geom& g, const void* q, const void* k, const void* v,
+                                     float* q_mean, float* k_mean, void* qpack, void* kpack, void* vpack,
+                                     float* q_sics, float* k_sics, hipStream_t s);
 // scheme generation: aggregate SICS of candidate c for every (b, h) from the
 // per-block SICS of Q and K, and the head-wise argmax over the candidates
 hipError_t launch_scheme_aggregate(const Geom& g, const float* q_sics, const float* k_sics, int c,

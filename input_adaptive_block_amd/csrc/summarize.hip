@@ -324,6 +324,15 @@ hipError_t launch_summarize_sics(const Geom& g, bool bf16, const void* q, const 
 #undef SPADE_SICS_LAUNCH
 }
 
+hipError_t launch_summarize_pack_sics(const Geom& g, const void* q, const void* k, const void* v,
+                                     float* q_mean, float* k_mean, void* qpack, void* kpack, void* vpack,
+                                     float* q_sics, float* k_sics, hipStream_t s) {
+  if (g.BH == 0) return hipSuccess;
+  if (g.d == 128)
+    return launch_t<true, 128, true, true>(g, q, k, v, q_mean, k_mean, qpack, kpack, vpack, 3, s, q_sics, k_sics);
+  return launch_t<true, 64, true, true>(g, q, k, v, q_mean, k_mean, qpack, kpack, vpack, 3, s, q_sics, k_sics);
+}
+
 hipError_t launch_summarize(const Geom& g, bool bf16, const void* q, const void* k, const void* v,
                             float* q_mean, float* k_mean, void* qpack, void* kpack, void* vpack,
                             hipStream_t s) {

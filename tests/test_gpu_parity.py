@@ -645,6 +645,10 @@ def test_attn_schemes_matches_oracle_and_single_scheme_runs(name):
     o, scheme, agg = spade.attn_schemes(q, k, v, grid, cands, cfg.mode, cfg.per_head_budget())
     torch.cuda.synchronize()
     sch = scheme.cpu().numpy()
+    # the choice equals the selection-only call's bit for bit (there, every
+    # candidate's SICS come from a SICS-only pass)
+    agg_s, scheme_s = spade.scheme_select(q, k, grid, cands)
+    assert torch.equal(agg, agg_s) and torch.equal(scheme, scheme_s)
     # per head: bit for bit the single-scheme run with that head's blocking
     for c, blk in enumerate(cands):
         oc, _, _ = spade.attn(q, k, v, grid, blk, cfg.mode, cfg.per_head_budget())
@@ -660,6 +664,40 @@ def test_attn_schemes_matches_oracle_and_single_scheme_runs(name):
     tol = BF16_TOL if cfg.dtype == "bf16" else F32_TOL
     of = dev_to_f64(o)
     assert np.abs(of[same] - ref[same]).max() <= tol
+
+
+@pytest.mark.parametrize("name,summarizer", [("mid_shape", "mean"), ("ragged_small", "max"), ("tail24", "min"),
+                                             ("d64", "mean"), ("big_block", "mean")])
+def test_fused_pack_pass_sics_equal_the_sics_pass(name, summarizer):
+    """spade_attn_schemes takes candidate 0's per-block SICS from the pass
+    that also summarizes and packs Q/K/V.  With one candidate its workspace
+    keeps them at the end (after the fp64 aggregates, 256-byte aligned):
+    they equal spade_summarize_sics's bit for bit."""
+    from input_adaptive_block_amd import _lib
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    p = spade.problem_for(q, grid, block, summarizer=summarizer)
+    bud = spade.Budget(cfg.mode, cfg.per_head_budget())
+    n = spade.spade_schemes_workspace_bytes(p, [block], bud)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    agg = torch.empty(1, cfg.B, cfg.H, dtype=torch.float32, device="cuda")
+    scheme = torch.empty(cfg.B, cfg.H, dtype=torch.int32, device="cuda")
+    _lib.spade_attn_schemes(p, q, k, v, [block], bud, o, agg, scheme, ws, n)
+    torch.cuda.synchronize()
+    BH, nblk = cfg.B * cfg.H, spade.spade_num_blocks(p)
+    a256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    q_off = a256(8 * BH)
+    k_off = q_off + a256(4 * BH * nblk)
+    fused_q = ws[q_off:q_off + 4 * BH * nblk].view(torch.float32).view(cfg.B, cfg.H, nblk)
+    fused_k = ws[k_off:k_off + 4 * BH * nblk].view(torch.float32).view(cfg.B, cfg.H, nblk)
+    _, _, qs, ks = spade.summarize_sics(q, k, grid, block, summarizer)
+    assert torch.equal(fused_q, qs) and torch.equal(fused_k, ks)
+    # and the output is the plain path's
+    o_plain, _, _ = spade.attn(q, k, v, grid, block, cfg.mode, cfg.per_head_budget(), summarizer=summarizer)
+    assert torch.equal(o, o_plain)
 
 
 @pytest.mark.parametrize("name,window,summarizer", [("mid_shape", (1, 1, 1), "max"), ("ragged_small", (0, 1, 0), "mean"),
