@@ -268,6 +268,13 @@ spade_status spade_attn_schemes(const spade_problem* p, const void* q, const voi
  * them with hipEventElapsedTime).  Pass NULLs to turn recording off. */
 void spade_profile_events(void* start, void* stop);
 
+/* Test hook (host only): which walk the bf16 attention kernel takes for this
+ * problem -- 1: the kept blocks' keys streamed back to back (every block a
+ * multiple of 8 tokens and at least 32, and a full block at least 16 keys
+ * short of whole 32-key subtiles), 0: each block padded to whole subtiles,
+ * -1: invalid problem. */
+int32_t spade_debug_dense_walk(const spade_problem* p);
+
 /* Test hook: the fp64 scores S [B, H, nblk, nblk] that estimate/select uses. */
 spade_status spade_debug_scores(const spade_problem* p, const float* q_mean, const float* k_mean,
                                 double* scores, void* stream);

@@ -15,7 +15,7 @@ from ._lib import (  # noqa: F401
     SPADE_KEEP_COUNT, SPADE_KEEP_MASS, SPADE_KEEP_RATIO, SPADE_OK, SPADE_ERR_CAPACITY,
     SPADE_ERR_DEVICE, SPADE_ERR_INVALID_ARG, SPADE_ERR_UNSUPPORTED, lib, spade_attn,
     spade_block_sparse_attn, spade_check, spade_debug_scores, spade_estimate_select,
-    spade_estimate_select_static, SPADE_STATIC_SCRATCH_BYTES,
+    spade_estimate_select_static, SPADE_STATIC_SCRATCH_BYTES, spade_debug_dense_walk,
     spade_attn_schemes, spade_max_nnz, spade_num_blocks, spade_profile_events, spade_scheme_select,
     spade_schemes_workspace_bytes, spade_summarize, spade_summarize_sics,
     spade_workspace_bytes,

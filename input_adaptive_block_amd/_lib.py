@@ -139,6 +139,7 @@ def _load() -> ctypes.CDLL:
         "spade_block_sparse_attn": (st, [P, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
         "spade_attn": (st, [P, vp, vp, vp, Bp, vp, vp, vp, i64, vp, sz, vp]),
         "spade_debug_scores": (st, [P, vp, vp, vp, vp]),
+        "spade_debug_dense_walk": (ctypes.c_int32, [P]),
         "spade_schemes_workspace_bytes": (sz, [P, vp, ctypes.c_int32, Bp]),
         "spade_scheme_select": (st, [P, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]),
         "spade_attn_schemes": (st, [P, vp, vp, vp, vp, ctypes.c_int32, Bp, vp, vp, vp, vp, sz, vp]),
@@ -157,7 +158,7 @@ EXPORTED = (
     "spade_num_blocks", "spade_max_nnz", "spade_workspace_bytes", "spade_check",
     "spade_status_string", "spade_summarize", "spade_summarize_sics", "spade_estimate_select",
     "spade_estimate_select_static",
-    "spade_block_sparse_attn", "spade_attn", "spade_debug_scores",
+    "spade_block_sparse_attn", "spade_attn", "spade_debug_scores", "spade_debug_dense_walk",
     "spade_profile_events",
     "spade_schemes_workspace_bytes", "spade_scheme_select", "spade_attn_schemes",
 )
@@ -230,6 +231,10 @@ def spade_estimate_select(problem: Problem, q_mean, k_mean, budget: Budget, row_
                                       ctypes.byref(budget.c()), _ptr(row_ptr), _ptr(col_idx),
                                       int(col_capacity), _ptr(workspace), int(ws_bytes), _stream(stream)),
            "spade_estimate_select")
+
+
+def spade_debug_dense_walk(problem: Problem) -> int:
+    return int(_LIB.spade_debug_dense_walk(ctypes.byref(problem.c())))
 
 
 def spade_estimate_select_static(problem: Problem, q_mean, k_mean, budget: Budget, row_ptr, col_idx,

@@ -51,6 +51,23 @@ spade_status make_geom(const spade_problem* p, Geom* g) {
   g->R = (int)R;
   g->bf16 = p->dtype == SPADE_BF16 ? 1 : 0;
   g->op = p->summarizer;
+  // dense key streaming: when padding a full block to whole 32-key subtiles
+  // would add at least 16 keys (72 -> 96, 40 -> 64; not 120 -> 128, where the
+  // padded walk is faster), and every block extent (full or edge) along each
+  // axis gives a multiple of 8 tokens, at least 32
+  {
+    const int ext[3][2] = {{bt, (int)(p->T % p->bt)}, {bh, (int)(p->Hh % p->bh)}, {bw, (int)(p->W % p->bw)}};
+    bool dense = p->dtype == SPADE_BF16 && P - ntok >= 16;
+    for (int a = 0; a < 2; ++a)
+      for (int b = 0; b < 2; ++b)
+        for (int c = 0; c < 2; ++c) {
+          const int et = ext[0][a], eh = ext[1][b], ew = ext[2][c];
+          if (et == 0 || eh == 0 || ew == 0) continue;  // no edge along that axis
+          const int n = et * eh * ew;
+          if (n % 8 != 0 || n < 32) dense = false;
+        }
+    g->dense = dense ? 1 : 0;
+  }
   g->hsel = nullptr;
   g->hval = 0;
   return SPADE_OK;
@@ -389,6 +406,12 @@ spade_status spade_attn(const spade_problem* p, const void* q, const void* k, co
 void spade_profile_events(void* start, void* stop) {
   g_prof_start = (hipEvent_t)start;
   g_prof_stop = (hipEvent_t)stop;
+}
+
+int32_t spade_debug_dense_walk(const spade_problem* p) {
+  Geom g;
+  if (make_geom(p, &g) != SPADE_OK) return -1;
+  return g.dense;
 }
 
 spade_status spade_debug_scores(const spade_problem* p, const float* q_mean, const float* k_mean,

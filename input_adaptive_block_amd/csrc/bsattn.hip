@@ -142,12 +142,57 @@ __device__ inline void cursor_next(Cursor& c, const uint32_t* ul, const uint16_t
   }
 }
 
+// A walk over the unit's key stream when every block holds a multiple of 8
+// tokens and at least 32: the kept blocks' keys back to back, one 32-key
+// subtile at a time.  The subtile starts at key kb of union entry pos; when
+// fewer than 32 of that entry's keys remain (b = n - kb < 32), its other
+// keys are the first 32 - b of entry pos + 1.  The entry after pos is read
+// one entry ahead (ae, an; zero past the last entry).
+struct DCursor {
+  int pos;
+  int kb;
+  int word;  // entry pos: block id | mask of the unit's rows keeping it << 12
+  int n;     // entry pos: tokens (0 past the last entry)
+  uint32_t ae;
+  uint32_t an;
+};
+
+__device__ inline DCursor dcursor_start(const uint32_t* ul, const uint16_t* un, int cnt) {
+  DCursor c;
+  c.pos = 0;
+  c.kb = 0;
+  c.word = cnt > 0 ? __builtin_amdgcn_readfirstlane((int)ul[0]) : 0;
+  c.n = cnt > 0 ? __builtin_amdgcn_readfirstlane((int)un[0]) : 0;
+  c.ae = cnt > 1 ? ul[1] : 0u;
+  c.an = cnt > 1 ? un[1] : 0u;
+  return c;
+}
+
+__device__ inline void dcursor_next(DCursor& c, const uint32_t* ul, const uint16_t* un, int cnt) {
+  c.kb += 32;
+  if (c.kb >= c.n) {
+    c.kb -= c.n;
+    ++c.pos;
+    c.word = __builtin_amdgcn_readfirstlane((int)c.ae);
+    c.n = __builtin_amdgcn_readfirstlane((int)c.an);
+    const bool more = c.pos + 1 < cnt;
+    const int pa = more ? c.pos + 1 : 0;
+    c.ae = more ? ul[pa] : 0u;
+    c.an = more ? un[pa] : 0u;
+  }
+}
+
+// Key order of a streamed K subtile: operand row r holds key r with bits 2
+// and 3 swapped, so that the eight scores a lane turns into one P operand are
+// eight consecutive keys, the keys its V operand holds (one 8-key group).
+__device__ inline int dense_key_of_row(int r) { return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
 // s_waitcnt immediate on gfx9: vmcnt in bits 3:0
 // and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima (no wait).
 constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 
-template <int D>
+template <int D, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     Geom g, const uint16_t* __restrict__ qpack, const uint16_t* __restrict__ kpack,
     const uint16_t* __restrict__ vpack, const int* __restrict__ row_ptr, const int* __restrict__ col_idx,
@@ -297,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     // VE (a compile-time constant) is the number of each lane's 16 scores that
     // are real keys when that does not depend on the lane (12 for 24 valid
     // keys); VE = 0 masks the keys from kvalid when it is below 32.
-    auto step = [&](auto ve_c, int kvalid, int kx, int vx) __attribute__((always_inline)) {
+    auto step = [&](auto ve_c, int klo, int kvalid, int kx, int vx) __attribute__((always_inline)) {
       constexpr int VE = decltype(ve_c)::value;
       constexpr int NP = VE == 0 ? 8 : VE / 2;  // pairs of scores that can hold a real key
       const bf16x8* kl = reinterpret_cast<const bf16x8*>(ring + kx);
@@ -320,7 +365,18 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
       bf16x8 vr[3];
       vr[0] = vl[(2 * (0 % NM) + 0 / NM) * 64 + lane];
       vr[1] = vl[(2 * (1 % NM) + 1 / NM) * 64 + lane];
-      if (VE == 0 && kvalid < 32) {
+      if constexpr (DENSE) {
+        // keys outside [klo, kvalid) weigh nothing; key of element v:
+        // 16 (v/8) + 8 half + v%8
+        if (klo > 0 || kvalid < 32) {
+          const int lo = klo - 8 * half, hi = kvalid - 8 * half;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kv = 16 * (v >> 3) + (v & 7);
+            if (kv < lo || kv >= hi) sx[v] = -__builtin_huge_valf();
+          }
+        }
+      } else if (VE == 0 && kvalid < 32) {
         const int kk = kvalid - 4 * half;  // key of element v: 8 (v/4) + 4 half + v%4
 #pragma unroll
         for (int v = 0; v < 16; ++v)
@@ -406,28 +462,69 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
       __builtin_amdgcn_s_setprio(0);
     };
 
+    // Dense streaming: the stage's copies gather each lane's 16 bytes from the
+    // block holding its key (K rows in dense_key_of_row order, V in 8-key
+    // groups); wave w copies the chunks CPW w .. CPW w + CPW - 1 of the stage,
+    // all in one of its two subtiles.  Advances k by the stage's two subtiles.
+    auto dissue = [&](DCursor& k, int slot) __attribute__((always_inline)) {
+      constexpr int CPS = D / 16;  // 1 KB chunks per subtile and tensor
+      const int t0 = wave * CPW;
+      const int sg = t0 / CPS;     // this wave's subtile of the stage (uniform)
+      int blkA = 0, kbA = 0, b = 32, blkB = 0;
+      bool valid = false;
+      auto grab = [&]() __attribute__((always_inline)) {
+        valid = k.pos < ucnt;
+        blkA = k.word & 0xFFF;
+        kbA = k.kb;
+        b = k.n - k.kb;
+        blkB = b < 32 ? (__builtin_amdgcn_readfirstlane((int)k.ae) & 0xFFF) : blkA;
+      };
+      if (sg == 0) grab();
+      dcursor_next(k, ulist, ublkn, ucnt);
+      if (sg == 1) grab();
+      dcursor_next(k, ulist, ublkn, ucnt);
+      if (!valid) {  // past the stream's end: any in-bounds tile (never computed)
+        blkA = 0;
+        kbA = 0;
+        b = 32;
+        blkB = 0;
+      }
+      const int r = lane & 31, h = lane >> 5;
+      const int key = dense_key_of_row(r);
+      const bool kin_b = key >= b;
+      const int kk = kin_b ? key - b : kbA + key;
+      const size_t ksrc = head_off + (size_t)(kin_b ? blkB : blkA) * g.P * D + (size_t)(kk >> 5) * SUB +
+                          (size_t)((kk & 31) + 32 * h) * 8;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const int ch = (t0 + c) % CPS;  // K channel chunk; V chunk 2 m + kc
+        const uint32_t kd = __builtin_amdgcn_readfirstlane(ring_lds + (uint32_t)(slot * 4 * SUB + sg * SUB + ch * 512) * 2u);
+        const uint32_t vd = kd + 2 * SUB * 2;
+        const int k8 = 16 * (ch & 1) + 8 * h;  // first of the lane's eight V keys
+        const bool vin_b = k8 >= b;
+        const int vk = vin_b ? k8 - b : kbA + k8;
+        const size_t vsrc = head_off + (size_t)(vin_b ? blkB : blkA) * g.P * D + (size_t)(vk >> 5) * SUB +
+                            (size_t)(((ch >> 1) * 2 + ((vk >> 4) & 1)) * 64 + ((vk >> 3) & 1) * 32 + r) * 8;
+        const char* kg = reinterpret_cast<const char*>(kpack + ksrc) + ch * 1024;
+        const char* vg = reinterpret_cast<const char*>(vpack + vsrc);
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(kg), "s"(kd) : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vg), "s"(vd) : "memory", "m0");
+      }
+    };
+
     // ---- stage ring of four slots: stage s is computed from slot s % 4
     // while stages s+1 and s+2 are in flight, and stage s+3 is issued at its
     // end; one barrier per stage ----
     // Every wave walks the stages it computes (cc); the copying waves also
     // walk the stages they copy (kc), three ahead.
     const bool copier = wave < kCopyWaves;
-    Cursor cc = cursor_start(ulist, ublkn, ucnt);
-    Cursor kc = cc;
     int si = 0;      // stage computed next
     int issued = 0;  // stages this copying wave has issued
-    if (copier) {
-      for (int p = 0; p < 3 && kc.pos < ucnt; ++p) {
-        issue(kc, issued & 3);
-        ++issued;
-        cursor_next(kc, ulist, ublkn, ucnt);
-      }
-    }
     bool did_prev = true;  // no LDS reads of this unit are outstanding yet
-    while (cc.pos < ucnt) {
-      // own copies of this stage have landed (those of the next two may still
-      // fly); a wave that skipped the previous stage may still have reads of
-      // the slot about to be refilled outstanding
+    // own copies of stage si have landed (those of the next two may still
+    // fly); a wave that skipped the previous stage may still have reads of
+    // the slot about to be refilled outstanding
+    auto stage_wait = [&]() __attribute__((always_inline)) {
       if (copier) {
         const int fly = issued - si - 1;
         if (__builtin_expect(fly >= 2 && did_prev, 1)) {
@@ -448,37 +545,91 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      did_prev = active && ((cc.word >> (12 + my_row)) & 1);
-      if (did_prev) {
-        const int kb = (si & 3) * 4 * SUB;
-        using k24_t = std::integral_constant<int, 12>;
-        using any_t = std::integral_constant<int, 0>;
-        // the stage's first subtile, then its second through the same code,
-        // unless the second holds 24 keys (the last subtile of a 120-token
-        // block), which has a step of its own
-        const int nk = cc.n - 32 * cc.s0;
-        int kx = kb, kv = min(32, nk), rest = nk - 32;
-        for (;;) {
-          step(any_t{}, kv, kx, kx + 2 * SUB);
-          if (rest <= 0) break;
-          if (rest == 24) {
-            step(k24_t{}, 24, kb + SUB, kb + 3 * SUB);
-            break;
-          }
-          kx = kb + SUB;
-          kv = min(32, rest);
-          rest = 0;
+    };
+    using any_t = std::integral_constant<int, 0>;
+    if constexpr (!DENSE) {
+      Cursor cc = cursor_start(ulist, ublkn, ucnt);
+      Cursor kc = cc;
+      if (copier) {
+        for (int p = 0; p < 3 && kc.pos < ucnt; ++p) {
+          issue(kc, issued & 3);
+          ++issued;
+          cursor_next(kc, ulist, ublkn, ucnt);
         }
       }
-      // stage s+3 goes into the slot of stage s-1, which every wave left
-      // before the barrier above
-      if (copier && kc.pos < ucnt) {
-        issue(kc, issued & 3);
-        ++issued;
-        cursor_next(kc, ulist, ublkn, ucnt);
+      while (cc.pos < ucnt) {
+        stage_wait();
+        did_prev = active && ((cc.word >> (12 + my_row)) & 1);
+        if (did_prev) {
+          const int kb = (si & 3) * 4 * SUB;
+          using k24_t = std::integral_constant<int, 12>;
+          // the stage's first subtile, then its second through the same code,
+          // unless the second holds 24 keys (the last subtile of a 120-token
+          // block), which has a step of its own
+          const int nk = cc.n - 32 * cc.s0;
+          int kx = kb, kv = min(32, nk), rest = nk - 32;
+          for (;;) {
+            step(any_t{}, 0, kv, kx, kx + 2 * SUB);
+            if (rest <= 0) break;
+            if (rest == 24) {
+              step(k24_t{}, 0, 24, kb + SUB, kb + 3 * SUB);
+              break;
+            }
+            kx = kb + SUB;
+            kv = min(32, rest);
+            rest = 0;
+          }
+        }
+        // stage s+3 goes into the slot of stage s-1, which every wave left
+        // before the barrier above
+        if (copier && kc.pos < ucnt) {
+          issue(kc, issued & 3);
+          ++issued;
+          cursor_next(kc, ulist, ublkn, ucnt);
+        }
+        cursor_next(cc, ulist, ublkn, ucnt);
+        ++si;
       }
-      cursor_next(cc, ulist, ublkn, ucnt);
-      ++si;
+    } else {
+      DCursor cc = dcursor_start(ulist, ublkn, ucnt);
+      DCursor kc = cc;
+      if (copier) {
+        for (int p = 0; p < 3 && kc.pos < ucnt; ++p) {
+          dissue(kc, issued & 3);
+          ++issued;
+        }
+      }
+      while (cc.pos < ucnt) {
+        stage_wait();
+        const int kb = (si & 3) * 4 * SUB;
+        did_prev = false;
+        // the stage's two subtiles through one copy of the step: this row's
+        // keys of each are the part of entry pos (keys [0, b)) and of entry
+        // pos + 1 (keys [b, 32)) that the row keeps
+#pragma unroll 1
+        for (int sg = 0; sg < 2; ++sg) {
+          if (active && cc.pos < ucnt) {
+            const int b = cc.n - cc.kb;
+            const bool keep_a = (cc.word >> (12 + my_row)) & 1;
+            int lo = 0, hi = keep_a ? 32 : 0;
+            if (b < 32) {
+              const bool keep_b = (__builtin_amdgcn_readfirstlane((int)cc.ae) >> (12 + my_row)) & 1;
+              lo = keep_a ? 0 : b;
+              hi = keep_b ? 32 : (keep_a ? b : 0);
+            }
+            if (lo < hi) {
+              step(any_t{}, lo, hi, kb + sg * SUB, kb + (2 + sg) * SUB);
+              did_prev = true;
+            }
+          }
+          dcursor_next(cc, ulist, ublkn, ucnt);
+        }
+        if (copier && kc.pos < ucnt) {
+          dissue(kc, issued & 3);
+          ++issued;
+        }
+        ++si;
+      }
     }
 
     if (active) {
@@ -607,14 +758,18 @@ hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpac
   if (grid > U) grid = U;
   if (grid < 1) grid = 1;
   const float scale_log2 = scale * 1.4426950408889634f;
-  if (g.d == 128)
-    bsattn_bf16_kernel<128><<<grid, kThreads, 0, s>>>(
-        g, (const uint16_t*)qpack, (const uint16_t*)kpack, (const uint16_t*)vpack, row_ptr, col_idx,
-        col_capacity, scale_log2, (uint16_t*)o, counter, U);
-  else
-    bsattn_bf16_kernel<64><<<grid, kThreads, 0, s>>>(
-        g, (const uint16_t*)qpack, (const uint16_t*)kpack, (const uint16_t*)vpack, row_ptr, col_idx,
-        col_capacity, scale_log2, (uint16_t*)o, counter, U);
+#define SPADE_BSATTN(DD, DN)                                                                                  \
+  bsattn_bf16_kernel<DD, DN><<<grid, kThreads, 0, s>>>(g, (const uint16_t*)qpack, (const uint16_t*)kpack,           \
+                                                     (const uint16_t*)vpack, row_ptr, col_idx, col_capacity,      \
+                                                     scale_log2, (uint16_t*)o, counter, U)
+  if (g.d == 128) {
+    if (g.dense) SPADE_BSATTN(128, true);
+    else SPADE_BSATTN(128, false);
+  } else {
+    if (g.dense) SPADE_BSATTN(64, true);
+    else SPADE_BSATTN(64, false);
+  }
+#undef SPADE_BSATTN
   return hipGetLastError();
 }
 

@@ -25,6 +25,12 @@ struct Geom {
   int R;      // B*H*nblk selection rows
   int bf16;   // 1: bf16 tensors (packed MFMA tiles), 0: fp32 debug path
   int op;     // block summarizer: 0 mean, 1 max, 2 min
+  // 1 when every block (partial edge blocks included) holds a multiple of 8
+  // tokens and at least 32, and padding a full block to whole 32-key subtiles
+  // would add 16 keys or more (bf16 only): attention streams the kept blocks'
+  // keys back to back instead, and V tiles are packed with eight consecutive
+  // keys per 16-byte vector
+  int dense;
   // head filter of a scheme's launch segment: when hsel is set, only the
   // (b, h) pairs with hsel[b*H + h] == hval are computed (device array)
   const int* hsel;

@@ -226,8 +226,11 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int e0 = 2 * e2, e1 = 2 * e2 + 1;
-          const int k0 = 32 * s + 16 * kc + 8 * (e0 >> 2) + 4 * (L >> 5) + (e0 & 3);
-          const int k1 = 32 * s + 16 * kc + 8 * (e1 >> 2) + 4 * (L >> 5) + (e1 & 3);
+          // keys of the lane's eight values: the order of the attention
+          // kernel's P operand (eight consecutive keys when streaming densely)
+          const int k0 = g.dense ? 32 * s + 16 * kc + 8 * (L >> 5) + e0
+                                 : 32 * s + 16 * kc + 8 * (e0 >> 2) + 4 * (L >> 5) + (e0 & 3);
+          const int k1 = g.dense ? k0 + 1 : 32 * s + 16 * kc + 8 * (e1 >> 2) + 4 * (L >> 5) + (e1 & 3);
           w[e2] = (uint32_t)vt[k0 * VROW + ch] | ((uint32_t)vt[k1 * VROW + ch] << 16);
         }
         const size_t sub_base = (size_t)((base >> 5) + s) * 32 * D;

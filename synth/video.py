@@ -163,6 +163,21 @@ TEST_CONFIGS = {
     "tail24": Config("tail24", B=1, H=2, d=128, T=4, Hh=8, W=17, bt=2, bh=4, bw=7,
                      dtype="bf16", sigma=0.5, amp_kind="uniform", amp_params=(0.3, 2.0),
                      mode=MODE_MASS, budget=(0.7,), seed=23),
+    # 120-token blocks and no partial block (3 x 3 x 3 blocks), hot blocks.
+    "mid_full": Config("mid_full", B=1, H=2, d=128, T=9, Hh=15, W=24, bt=3, bh=5, bw=8,
+                       dtype="bf16", sigma=0.5, amp_kind="uniform", amp_params=(0.3, 2.0),
+                       mode=MODE_MASS, budget=(0.9,), seed=24, hot_frac=0.1, hot_offset=3.0),
+    # Blocks whose tokens are a multiple of 8 (at least 32) everywhere but
+    # would waste 16 or more keys padded to 32-key subtiles, so attention
+    # streams the kept blocks' keys back to back: 72- and 40-token blocks
+    # (partial along w; subtiles straddle block boundaries) ...
+    "dense_mixed": Config("dense_mixed", B=1, H=3, d=128, T=6, Hh=12, W=23, bt=2, bh=4, bw=9,
+                          dtype="bf16", sigma=0.5, amp_kind="uniform", amp_params=(0.3, 2.0),
+                          mode=MODE_RATIO, budget=(0.4,), seed=25),
+    # ... and 40-token blocks at head dimension 64, two batches.
+    "dense_40": Config("dense_40", B=2, H=2, d=64, T=4, Hh=10, W=24, bt=1, bh=5, bw=8,
+                       dtype="bf16", sigma=0.5, amp_kind="uniform", amp_params=(0.3, 2.0),
+                       mode=MODE_MASS, budget=(0.8,), seed=26),
     # fp32 (debug) path on a ragged shape.
     "ragged_f32": Config("ragged_f32", B=1, H=2, d=128, T=5, Hh=7, W=9, bt=4, bh=4, bw=4,
                          dtype="f32", sigma=1.0, amp_kind="const", amp_params=(0.0,),

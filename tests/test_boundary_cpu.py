@@ -331,3 +331,17 @@ def test_static_select_rejects_before_device():
     with pytest.raises(spade.SpadeError) as e:
         spade.spade_estimate_select_static(q, 0, 0, bw, 1, 1, spade.spade_max_nnz(q, bw), stream=0)
     assert e.value.status == CAP
+
+
+@pytest.mark.parametrize("name,dense", [("small", 1), ("small_shape", 1), ("dense_mixed", 1), ("dense_40", 1),
+                                        ("mid", 0), ("large", 0), ("mid_full", 0), ("d64", 0), ("ragged", 0),
+                                        ("mid_shape", 0), ("tail24", 0), ("big_block", 0), ("tiny", 0),
+                                        ("tiny_bf16", 0), ("token_level", 0)])
+def test_attention_walk_by_block_shape(name, dense):
+    """Blocks of 72 or 40 tokens (every block a multiple of 8, at least 32)
+    are streamed back to back; 120-, 64-, 32- and 256-token blocks, shapes
+    with a partial block of 24, 60 or 16 tokens, and fp32 are padded to whole
+    32-key subtiles."""
+    cfg = synth.get_config(name)
+    assert spade.spade_debug_dense_walk(_prob(cfg)) == dense
+    assert spade.spade_debug_dense_walk(_prob(cfg, dtype=spade.SPADE_F32)) == 0

@@ -31,7 +31,7 @@ import input_adaptive_block_amd as spade  # noqa: E402
 BF16_TOL = 2e-2
 F32_TOL = 1e-5
 SMALL = ["tiny", "tiny_bf16", "ragged_p64", "mid_shape", "small_shape", "ragged_small", "big_block",
-         "token_level", "one_block", "d64", "tail24", "ragged_f32"]
+         "token_level", "one_block", "d64", "tail24", "ragged_f32", "mid_full", "dense_mixed", "dense_40"]
 
 
 # ---------------------------------------------------------------------------
@@ -161,7 +161,7 @@ def test_whole_path_with_max_min_summarizer(name, op):
 
 @pytest.mark.parametrize("window,scale_budget", [((0, 0, 0), 0.0), ((1, 1, 2), 0.0), ((1, 0, 1), 1.0),
                                                   ((2, 2, 2), 1.0)])
-@pytest.mark.parametrize("name", ["mid_shape", "ragged_small", "tiny", "d64"])
+@pytest.mark.parametrize("name", ["mid_shape", "ragged_small", "tiny", "d64", "dense_40"])
 def test_static_window_united_with_selection(name, window, scale_budget):
     """Budget 0 gives the static window alone; otherwise the window is united
     with the scored blocks.  Selection is checked row by row, attention on
@@ -360,7 +360,7 @@ def test_limits_selection_and_attention_match_oracle(name):
     assert err <= BF16_TOL, err
 
 
-@pytest.mark.parametrize("name", ["ragged_small", "ragged_p64", "tiny", "ragged_f32"])
+@pytest.mark.parametrize("name", ["ragged_small", "ragged_p64", "tiny", "ragged_f32", "mid_full", "dense_40"])
 def test_ratio_one_equals_dense_attention(name):
     cfg = synth.get_config(name)
     x = synth.make_inputs(cfg)
@@ -373,7 +373,7 @@ def test_ratio_one_equals_dense_attention(name):
     assert err <= (BF16_TOL if cfg.dtype == "bf16" else F32_TOL), err
 
 
-@pytest.mark.parametrize("name", ["mid_shape", "ragged_small", "tiny"])
+@pytest.mark.parametrize("name", ["mid_shape", "ragged_small", "tiny", "dense_mixed"])
 def test_block_sparse_attn_on_oracle_csr(name):
     """spade_block_sparse_attn alone, fed the oracle's own CSR."""
     cfg = synth.get_config(name)
@@ -391,7 +391,7 @@ def test_block_sparse_attn_on_oracle_csr(name):
     assert err <= (BF16_TOL if cfg.dtype == "bf16" else F32_TOL), err
 
 
-@pytest.mark.parametrize("name", ["mid_shape", "tiny"])
+@pytest.mark.parametrize("name", ["mid_shape", "tiny", "mid_full", "dense_mixed"])
 def test_arbitrary_csr_is_memory_safe(name):
     """A row is a set (repeated ids count once, order is free), invalid ids are
     skipped, empty rows give zeros."""
@@ -635,7 +635,7 @@ def test_scheme_choice_follows_constructed_fields():
     assert abs(a[0, 0, 0] - 1.0) < 1e-6 and abs(a[1, 0, 1] - 1.0) < 1e-6
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid_shape", "ragged_small", "ragged_f32"])
+@pytest.mark.parametrize("name", ["tiny", "mid_shape", "ragged_small", "ragged_f32", "mid_full", "dense_mixed"])
 def test_attn_schemes_matches_oracle_and_single_scheme_runs(name):
     cfg = synth.get_config(name)
     x = synth.make_inputs(cfg)
