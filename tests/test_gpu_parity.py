@@ -808,3 +808,47 @@ def test_single_candidate_equals_the_plain_path():
     assert (scheme == 0).all()
     assert torch.equal(o1, o0)
 
+
+
+@pytest.mark.parametrize("name", ["mid_full", "dense_mixed", "ragged_small"])
+def test_whole_path_in_a_hip_graph(name):
+    """The whole path (pack, estimate + select, chunked scan, compaction,
+    unit counter, attention) records into a HIP graph: every launch is a
+    kernel on the caller's stream, with no memset node and no host call.
+    Each of three replays, with eager work and synchronisations between
+    them, equals the eager call bit for bit."""
+    cfg = synth.get_config(name)
+    x = synth.make_inputs(cfg)
+    grid, block = grid_block(cfg)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    p = spade.problem_for(q, grid, block)
+    bud = spade.Budget(cfg.mode, cfg.per_head_budget())
+    cap = spade.spade_max_nnz(p, bud)
+    R = cfg.B * cfg.H * spade.spade_num_blocks(p)
+    ws = spade.alloc_workspace(p, q.device)
+    o_ref, rp_ref, ci_ref = spade.attn(q, k, v, grid, block, cfg.mode, cfg.per_head_budget())
+    o = torch.empty_like(q)
+    rp = torch.empty(R + 1, dtype=torch.int32, device="cuda")
+    ci = torch.empty(cap, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        spade.spade_attn(p, q, k, v, bud, o, rp, ci, cap, ws, ws.numel(), side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        spade.spade_attn(p, q, k, v, bud, o, rp, ci, cap, ws, ws.numel(), side)
+    nnz = int(rp_ref[-1])
+    for rep in range(3):
+        o.fill_(float("nan"))
+        ci.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(rp, rp_ref), rep
+        assert torch.equal(ci[:nnz], ci_ref[:nnz]), rep
+        assert torch.equal(o, o_ref), rep
+        # eager work between replays
+        spade.attn(q, k, v, grid, block, cfg.mode, cfg.per_head_budget())
+        torch.cuda.synchronize()

@@ -89,3 +89,33 @@ def test_static_scratch_rejects_oversize_problems():
     with pytest.raises(spade.SpadeError) as e:
         spade.estimate_select_static(qm, qm, p, "ratio", [0.1] * cfg.H)
     assert e.value.status == spade.SPADE_ERR_CAPACITY
+
+
+def test_static_scratch_under_graph_capture():
+    """The use the entry point exists for: recorded into a HIP graph (after
+    one eager call has looked up the device's buffer), its replays equal the
+    workspace entry point's CSR, with other selections run eagerly between
+    them."""
+    cfg = synth.get_config("small")
+    qm, km, p = _summaries(cfg)
+    per_head = cfg.per_head_budget()
+    ref = spade.estimate_select(qm, km, p, cfg.mode, per_head)
+    rp, ci = spade.estimate_select_static(qm, km, p, cfg.mode, per_head)  # eager, looks up the buffer
+    bud = spade.Budget(cfg.mode, per_head)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        spade.spade_estimate_select_static(p, qm, km, bud, rp, ci, ci.numel(), side)
+    other_q, other_k, other_p = _summaries(synth.get_config("mid_shape"))
+    for rep in range(3):
+        rp.fill_(-1)
+        ci.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _same_csr(ref, (rp, ci))
+        # another problem through the same static buffer, eagerly
+        spade.estimate_select_static(other_q, other_k, other_p, "count", [3] * other_p.H)
+        torch.cuda.synchronize()
