@@ -149,12 +149,17 @@ __device__ inline uint64_t order_key(double s) {
 // and xor 8 would, and the swaps those of xor 16 and xor 32: the steps add
 // the same operand pairs as a shuffle-xor butterfly, every lane ending with
 // the same bits, at VALU latency instead of LDS-permute latency.
+// (Every lane has a source in these patterns, so the moves need no old value.)
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t b) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
 template <int CTRL>
 __device__ inline double dpp_f64(double x) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, x);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
-  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+  return __builtin_bit_cast(double, dpp_u64<CTRL>(__builtin_bit_cast(uint64_t, x)));
 }
 
 // The two values a permlane swap leaves a lane: its own and its partner's
@@ -195,6 +200,27 @@ __device__ inline double wave_max(double x) {
   return fmax(a, b);
 }
 
+// The same butterfly for the bitwise OR and AND of 64-bit words.
+__device__ inline void wave_or_and(uint64_t& o, uint64_t& a) {
+  o |= dpp_u64<0xB1>(o);
+  a &= dpp_u64<0xB1>(a);
+  o |= dpp_u64<0x4E>(o);
+  a &= dpp_u64<0x4E>(a);
+  o |= dpp_u64<0x141>(o);
+  a &= dpp_u64<0x141>(a);
+  o |= dpp_u64<0x140>(o);
+  a &= dpp_u64<0x140>(a);
+  double x0, x1, y0, y1;
+  swap_f64<true>(__builtin_bit_cast(double, o), x0, x1);
+  swap_f64<true>(__builtin_bit_cast(double, a), y0, y1);
+  o = __builtin_bit_cast(uint64_t, x0) | __builtin_bit_cast(uint64_t, x1);
+  a = __builtin_bit_cast(uint64_t, y0) & __builtin_bit_cast(uint64_t, y1);
+  swap_f64<false>(__builtin_bit_cast(double, o), x0, x1);
+  swap_f64<false>(__builtin_bit_cast(double, a), y0, y1);
+  o = __builtin_bit_cast(uint64_t, x0) | __builtin_bit_cast(uint64_t, x1);
+  a = __builtin_bit_cast(uint64_t, y0) & __builtin_bit_cast(uint64_t, y1);
+}
+
 // lane l's double (l uniform)
 __device__ inline double read_lane_f64(double x, int l) {
   const uint64_t u = __builtin_bit_cast(uint64_t, x);
@@ -226,6 +252,36 @@ __device__ inline bool isolated_threshold(const uint64_t (&key)[E], int bit, uin
     }
   }
   return true;
+}
+
+// In the mass search below, the candidates at bit b are the real keys that
+// share the bits above b fixed in T.  Wherever they all agree, the
+// threshold's bit follows without a mass test: a common 1 keeps every
+// candidate at or above the tested value (the same set of keys as T itself,
+// whose mass reaches the target), a common 0 puts every candidate below it
+// (the same set as the last test that failed).  So T takes the candidates'
+// common bits b .. d+1, d the highest bit where they differ, and the search
+// resumes at d; -1 when they agree on every bit (T is then their key).
+template <int E>
+__device__ inline int skip_common_bits(const uint64_t (&key)[E], int nK, int lane, uint64_t& T, int b) {
+  const uint64_t low = b >= 63 ? ~0ull : ((2ull << b) - 1ull);  // bits b .. 0
+  uint64_t o = 0ull, a = ~0ull;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool cand = 64 * e + lane < nK && ((key[e] ^ T) & ~low) == 0ull;
+    o |= cand ? key[e] : 0ull;
+    a &= cand ? key[e] : ~0ull;
+  }
+  wave_or_and(o, a);
+  const uint64_t diff = (o ^ a) & low;
+  if (diff == 0ull) {
+    T = (T & ~low) | (o & low);
+    return -1;
+  }
+  const int d = 63 - __builtin_clzll(diff);
+  const uint64_t common = low & ~((2ull << d) - 1ull);  // bits b .. d+1
+  T = (T & ~common) | (o & common);
+  return d;
 }
 
 // The score an order key encodes (order_key is a bijection on doubles).
@@ -286,12 +342,24 @@ __device__ inline void select_row(const Geom& g, const SelectArgs& a, int row, i
     // non-increasing in T because every partial sum only drops non-negative
     // terms when T grows
     uint64_t T = 0ull;
-    for (int bit = 63; bit >= 0; --bit) {
+    // common bits are skipped before the first test (all real keys are
+    // candidates) and after it (the candidates then share the sign bit, and
+    // mostly the exponent's high bits too); with a target of 0 every test
+    // passes and no key is kept by score
+    const bool skip = target > 0.0;
+    int bit = skip ? skip_common_bits(key, nK, lane, T, 63) : 63;
+    bool tested = false;
+    for (; bit >= 0; --bit) {
       const uint64_t cand = T | (1ull << bit);
       double f = 0.0;
 #pragma unroll
       for (int e = 0; e < E; ++e) f += (key[e] >= cand) ? p[e] : 0.0;
       if (wave_sum(f) >= target) T = cand;
+      if (skip && !tested && bit > 0) {
+        tested = true;
+        bit = skip_common_bits(key, nK, lane, T, bit - 1) + 1;  // the loop steps to the returned bit
+        continue;
+      }
       if ((bit & 3) == 0 && bit > 0 && isolated_threshold(key, bit, T)) break;
     }
     double f = 0.0;
