@@ -72,9 +72,12 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(flops_launch):
+def load_traffic(workload_is_mid):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source."""
+    summary of the mid layer, if this run is that workload and the counters
+    were taken on the current kernel source."""
+    if not workload_is_mid:
+        return None
     path = os.path.join(ROOT, "profiles", "bsattn_mid_traffic.json")
     try:
         with open(path) as f:
@@ -279,7 +282,7 @@ def main():
     summ_bytes = 2 * q.numel() * q.element_size() + 2 * qm.numel() * 4
 
     achieved = flops / (attn_avg * 1e-3) / 1e12
-    traffic = load_traffic(flops)
+    traffic = load_traffic(cfg.name == "mid" and args.ratio is None)
     result = {
         "metric": "block-sparse attn ms/layer + effective TFLOPS (frac of bf16 MFMA peak) at 75K tok",
         "value": flops / (ms_per_step * 1e-3) / 1e12,
