@@ -49,6 +49,15 @@
 // * A wavefront raises its issue priority for its runs of MFMAs, so a wave
 //   that reaches its MFMAs keeps the matrix pipe while the others run their
 //   softmax arithmetic beside it.
+// * Blocks that pad badly to 32-key subtiles (every block a multiple of 8
+//   tokens, at least 32, and a full block 16 or more keys short of whole
+//   subtiles, e.g. 72 -> 96) are walked densely instead: the unit's union is
+//   one key stream cut into 32-key subtiles that may straddle two blocks.
+//   Each lane's 16-byte copy is gathered from the block holding its key; K
+//   rows are loaded with bits 2 and 3 of the key swapped and V is packed in
+//   8-key groups, so that a lane's P operand and V operand hold the same
+//   eight consecutive keys; a row computes the part of a subtile its kept
+//   blocks cover, under a key-range mask.
 // * fp32 online softmax in the exp2 domain with log2(e) folded into the scale;
 //   the running max only moves when a score exceeds it by more than 2^8, which
 //   bounds every p by 256 (exact in value, fewer rescales of the 64-register O
