@@ -281,6 +281,29 @@ def main():
     bsa_ms = timed(lambda: spade.spade_block_sparse_attn(p, q, k, v, rp, ci, cap, o2, ws, ws.numel(), stream))
     summ_bytes = 2 * q.numel() * q.element_size() + 2 * qm.numel() * 4
 
+    # the attention kernel once more over the same kept pairs, on all-zero Q, K
+    # and V: the same instructions (the running max moves once per query), but
+    # operands that do not toggle, so the part holds a higher clock under its
+    # power limit; the ratio of the two times is the ratio of the clocks
+    def attn_events(qq, kk, vv, reps=5):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            spade.spade_profile_events(a.cuda_event, b.cuda_event)
+            spade.spade_block_sparse_attn(p, qq, kk, vv, rp, ci, cap, o2, ws, ws.numel(), stream)
+            spade.spade_profile_events(None, None)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.mean(ts))
+
+    attn_same_ms = attn_events(q, k, v)
+    zq, zk, zv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    attn_zero_ms = attn_events(zq, zk, zv)
+    del zq, zk, zv
+
     achieved = flops / (attn_avg * 1e-3) / 1e12
     traffic = load_traffic(cfg.name == "mid" and args.ratio is None)
     result = {
@@ -319,6 +342,8 @@ def main():
             "estimate_select": sel_ms,
             "block_sparse_attn_call": bsa_ms,
             "attention_kernel": attn_avg,
+            "attention_kernel_again": attn_same_ms,
+            "attention_kernel_zero_qkv": attn_zero_ms,
             "non_attention_share_of_step": 1.0 - attn_avg / ms_per_step,
         },
         "roofline": {
