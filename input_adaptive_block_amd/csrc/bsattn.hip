@@ -466,6 +466,9 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
 #pragma unroll
         for (int e = (i - NM) * 8 / NM; e < (i - NM + 1) * 8 / NM; ++e)
           if (e < NP) lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], kOnes2, lsum, false);
+        // keeps the row-sum terms beside this MFMA: without it the compiler
+        // sinks the whole chain of dependent dot2s past the end of the step
+        asm volatile("" : "+v"(lsum));
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
