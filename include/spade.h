@@ -32,7 +32,9 @@
  *   held until the process ends) that spade_estimate_select_static uses.
  * - The workspace holds per-call scratch (summaries, scores, packed operand
  *   tiles, the attention kernel's unit counter): calls that may run at the same time,
- *   on one stream or several, each need a workspace of their own.
+ *   on one stream or several, each need a workspace of their own.  It must
+ *   start on a 256-byte boundary (as hipMalloc returns); a misaligned
+ *   workspace is rejected with SPADE_ERR_INVALID_ARG.
  * - Every compute call validates its arguments on the host first; on any
  *   error it returns a status and launches nothing.  Launches are
  *   asynchronous on `stream` (a hipStream_t; NULL = the default stream); the

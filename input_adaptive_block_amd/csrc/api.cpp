@@ -196,9 +196,15 @@ SelectArgs make_select_args(const spade_budget* bgt, const Geom& g) {
 
 char* ws_ptr(void* ws, size_t off) { return reinterpret_cast<char*>(ws) + off; }
 
+// every workspace region starts on a 256-byte boundary of the workspace, and
+// the kernels read and write them with 16-byte accesses
+bool misaligned(const void* ws) { return (reinterpret_cast<uintptr_t>(ws) & 255u) != 0; }
+
+// attn_counter: the attention kernel's unit counter, cleared by the last
+// kernel of the selection when an attention launch follows (else null)
 spade_status run_select(const spade_problem* p, const Geom& g, const Workspace& L, const float* qm,
                         const float* km, const spade_budget* bgt, int* row_ptr, int* col_idx, void* ws,
-                        hipStream_t s) {
+                        int* attn_counter, hipStream_t s) {
   int* counts = reinterpret_cast<int*>(ws_ptr(ws, L.counts));
   uint32_t* mask = reinterpret_cast<uint32_t*>(ws_ptr(ws, L.mask));
   const SelectArgs a = make_select_args(bgt, g);
@@ -210,9 +216,8 @@ spade_status run_select(const spade_problem* p, const Geom& g, const Workspace& 
     SPADE_TRY(dev(launch_scores(g, qm, km, est_scale(p), scores, s)));
     SPADE_TRY(dev(launch_select(g, scores, a, counts, mask, L.mask_words, s)));
   }
-  SPADE_TRY(dev(launch_scan(g, counts, row_ptr, reinterpret_cast<int*>(ws_ptr(ws, L.scan)), s)));
-  SPADE_TRY(dev(launch_compact(g, row_ptr, mask, L.mask_words, col_idx, s)));
-  return SPADE_OK;
+  return dev(launch_csr(g, counts, mask, L.mask_words, row_ptr, col_idx,
+                        reinterpret_cast<int*>(ws_ptr(ws, L.scan)), attn_counter, s));
 }
 
 }  // namespace
@@ -258,8 +263,8 @@ spade_status estimate_select_entry(const spade_problem* p, const float* q_mean, 
   if (g.R == 0) return dev(launch_scan(g, nullptr, row_ptr, nullptr, s));
   if (!q_mean || !k_mean || !col_idx) return SPADE_ERR_INVALID_ARG;
   if (lookup) SPADE_TRY(dev(lookup(&ws)));
-  if (!ws) return SPADE_ERR_INVALID_ARG;
-  return run_select(p, g, L, q_mean, k_mean, budget, row_ptr, col_idx, ws, s);
+  if (!ws || misaligned(ws)) return SPADE_ERR_INVALID_ARG;
+  return run_select(p, g, L, q_mean, k_mean, budget, row_ptr, col_idx, ws, nullptr, s);
 }
 
 }  // namespace spade
@@ -346,7 +351,7 @@ spade_status spade_block_sparse_attn(const spade_problem* p, const void* q, cons
   const Workspace L = workspace_layout(g);
   if (ws_bytes < L.total) return SPADE_ERR_CAPACITY;
   if (g.R == 0) return SPADE_OK;
-  if (!q || !k || !v || !row_ptr || !o || !workspace) return SPADE_ERR_INVALID_ARG;
+  if (!q || !k || !v || !row_ptr || !o || !workspace || misaligned(workspace)) return SPADE_ERR_INVALID_ARG;
   if (col_capacity > 0 && !col_idx) return SPADE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   const float scale = attn_scale(p);
@@ -357,7 +362,7 @@ spade_status spade_block_sparse_attn(const spade_problem* p, const void* q, cons
     SPADE_TRY(dev(launch_summarize(g, true, q, k, v, nullptr, nullptr, qp, kp, vp, s)));
     return timed_attention(s, [&] {
       return launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o,
-                                reinterpret_cast<int*>(ws_ptr(workspace, L.counter)), num_cus(), s);
+                                reinterpret_cast<int*>(ws_ptr(workspace, L.counter)), false, num_cus(), s);
     });
   }
   return timed_attention(s, [&] {
@@ -380,7 +385,7 @@ spade_status spade_attn(const spade_problem* p, const void* q, const void* k, co
   if (!row_ptr) return SPADE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   if (g.R == 0) return dev(launch_scan(g, nullptr, row_ptr, nullptr, s));
-  if (!q || !k || !v || !o || !col_idx || !workspace) return SPADE_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !col_idx || !workspace || misaligned(workspace)) return SPADE_ERR_INVALID_ARG;
   float* qm = reinterpret_cast<float*>(ws_ptr(workspace, L.qmean));
   float* km = reinterpret_cast<float*>(ws_ptr(workspace, L.kmean));
   const float scale = attn_scale(p);
@@ -389,14 +394,15 @@ spade_status spade_attn(const spade_problem* p, const void* q, const void* k, co
     void* kp = ws_ptr(workspace, L.kpack);
     void* vp = ws_ptr(workspace, L.vpack);
     SPADE_TRY(dev(launch_summarize(g, true, q, k, v, qm, km, qp, kp, vp, s)));
-    SPADE_TRY(run_select(p, g, L, qm, km, budget, row_ptr, col_idx, workspace, s));
+    int* counter = reinterpret_cast<int*>(ws_ptr(workspace, L.counter));
+    SPADE_TRY(run_select(p, g, L, qm, km, budget, row_ptr, col_idx, workspace, counter, s));
     return timed_attention(s, [&] {
-      return launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o,
-                                reinterpret_cast<int*>(ws_ptr(workspace, L.counter)), num_cus(), s);
+      return launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, col_capacity, scale, o, counter, true,
+                                num_cus(), s);
     });
   }
   SPADE_TRY(dev(launch_summarize(g, false, q, k, nullptr, qm, km, nullptr, nullptr, nullptr, s)));
-  SPADE_TRY(run_select(p, g, L, qm, km, budget, row_ptr, col_idx, workspace, s));
+  SPADE_TRY(run_select(p, g, L, qm, km, budget, row_ptr, col_idx, workspace, nullptr, s));
   return timed_attention(s, [&] {
     return launch_bsattn_f32(g, (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
                              col_capacity, scale, (float*)o, s);
@@ -535,7 +541,7 @@ spade_status spade_scheme_select(const spade_problem* p, const void* q, const vo
   SPADE_TRY(scheme_layout(gs, num_candidates, nullptr, &L));
   if (ws_bytes < L.total_select) return SPADE_ERR_CAPACITY;
   if (gs[0].BH == 0) return SPADE_OK;
-  if (!q || !k || !scheme || !workspace) return SPADE_ERR_INVALID_ARG;
+  if (!q || !k || !scheme || !workspace || misaligned(workspace)) return SPADE_ERR_INVALID_ARG;
   return run_scheme_select(p, gs, num_candidates, L, q, k, nullptr, nullptr, agg, scheme, workspace,
                            (hipStream_t)stream);
 }
@@ -551,7 +557,7 @@ spade_status spade_attn_schemes(const spade_problem* p, const void* q, const voi
   SPADE_TRY(scheme_layout(gs, num_candidates, budget, &L));
   if (ws_bytes < L.total_attn) return SPADE_ERR_CAPACITY;
   if (gs[0].BH == 0) return SPADE_OK;
-  if (!q || !k || !v || !o || !scheme || !workspace) return SPADE_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !scheme || !workspace || misaligned(workspace)) return SPADE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   void* pw = ws_ptr(workspace, L.pipe);
   SPADE_TRY(run_scheme_select(p, gs, num_candidates, L, q, k, v, pw, agg, scheme, workspace, s));
@@ -572,12 +578,13 @@ spade_status spade_attn_schemes(const spade_problem* p, const void* q, const voi
       void* vp = ws_ptr(pw, W.vpack);
       // candidate 0's tiles and means are already in place for every head
       if (c > 0) SPADE_TRY(dev(launch_summarize(g, true, q, k, v, qm, km, qp, kp, vp, s)));
-      SPADE_TRY(run_select(p, g, W, qm, km, budget, row_ptr, col_idx, pw, s));
-      SPADE_TRY(dev(launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, L.cap, scale, o,
-                                       reinterpret_cast<int*>(ws_ptr(pw, W.counter)), num_cus(), s)));
+      int* counter = reinterpret_cast<int*>(ws_ptr(pw, W.counter));
+      SPADE_TRY(run_select(p, g, W, qm, km, budget, row_ptr, col_idx, pw, counter, s));
+      SPADE_TRY(dev(launch_bsattn_bf16(g, qp, kp, vp, row_ptr, col_idx, L.cap, scale, o, counter, true,
+                                       num_cus(), s)));
     } else {
       SPADE_TRY(dev(launch_summarize(g, false, q, k, nullptr, qm, km, nullptr, nullptr, nullptr, s)));
-      SPADE_TRY(run_select(p, g, W, qm, km, budget, row_ptr, col_idx, pw, s));
+      SPADE_TRY(run_select(p, g, W, qm, km, budget, row_ptr, col_idx, pw, nullptr, s));
       SPADE_TRY(dev(launch_bsattn_f32(g, (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
                                       L.cap, scale, (float*)o, s)));
     }

@@ -759,13 +759,15 @@ __global__ __launch_bounds__(kF32Threads) void bsattn_f32_kernel(
 
 hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpack, const void* vpack,
                               const int* row_ptr, const int* col_idx, long long col_capacity, float scale,
-                              void* o, int* counter, int num_cus, hipStream_t s) {
+                              void* o, int* counter, bool counter_cleared, int num_cus, hipStream_t s) {
   if (g.R == 0) return hipSuccess;
   const UnitMap um = unit_map(g);
   const int U = g.BH * um.per_head;
-  counter_reset_kernel<<<1, 1, 0, s>>>(counter);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!counter_cleared) {
+    counter_reset_kernel<<<1, 1, 0, s>>>(counter);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   int grid = num_cus;  // one 12-wave workgroup per CU (LDS-limited)
   if (grid > U) grid = U;
   if (grid < 1) grid = 1;

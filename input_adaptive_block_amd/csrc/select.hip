@@ -18,9 +18,12 @@
 //                   ties to the lower block id.  Emits the kept set as a
 //                   bitmask and a count.  Rows wider than the LDS tile take
 //                   scores_kernel (S in HBM) + select_kernel, same arithmetic.
-//   chunk_sum / chunk_offsets / scan_apply
-//                   row_ptr = exclusive prefix sum of the counts, over chunks.
-//   compact_kernel  one wavefront per row writes the kept ids ascending.
+//   csr_build_kernel
+//                   (up to 32768 rows) row_ptr = exclusive prefix sum of the
+//                   counts and the kept ids ascending, in one kernel.
+//   chunk_sum / chunk_offsets / scan_apply, compact_kernel
+//                   the same for more rows: the prefix sum over chunks, then
+//                   one wavefront per row writes the kept ids ascending.
 #include "spade_internal.h"
 
 namespace spade {
@@ -53,10 +56,17 @@ __device__ inline void score_tiles(const float* __restrict__ qh, const float* __
   const float4* qrow = reinterpret_cast<const float4*>(qh + (size_t)min(row0 + li, nK - 1) * D + lk * NS);
 #pragma unroll
   for (int v = 0; v < NV; ++v) qa[v] = qrow[v];
-  for (int ct = ct0; ct < ntiles; ct += step) {
+  // the next tile's operands are loaded while this tile's MFMAs run (the row
+  // index is clamped, so the load past the last tile reads a valid row)
+  auto load_k = [&](float4 (&dst)[NV], int ct) __attribute__((always_inline)) {
     const float4* krow = reinterpret_cast<const float4*>(kh + (size_t)min(16 * ct + li, nK - 1) * D + lk * NS);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) kb[v] = krow[v];
+    for (int v = 0; v < NV; ++v) dst[v] = krow[v];
+  };
+  load_k(kb, ct0);
+  for (int ct = ct0; ct < ntiles; ct += step) {
+    float4 kn[NV];
+    load_k(kn, ct + step);
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -66,6 +76,8 @@ __device__ inline void score_tiles(const float* __restrict__ qh, const float* __
       acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[v].w, (double)kb[v].w, acc, 0, 0, 0);
     }
     f(ct, acc);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) kb[v] = kn[v];
   }
 }
 
@@ -620,11 +632,140 @@ __global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(int R, const i
 
 __global__ void zero_row_ptr_kernel(int* __restrict__ row_ptr) { row_ptr[0] = 0; }
 
+// Kept ids id0 + 32 w + b for the set bits b of bitmask words w < nwords,
+// held one per lane (word w in lane w, nwords <= 64), written ascending from
+// col_idx[out]; returns the position after the last.  For each 64 ids the two
+// words, made uniform with readlane, are the chunk's ballot.
+__device__ inline int compact_row_from_lanes(uint32_t word, int nwords, int lane, int out, int id0,
+                                             int* __restrict__ col_idx) {
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int w = 0; w < nwords; w += 2) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)word, w);
+    const uint32_t hi = w + 1 < nwords ? (uint32_t)__builtin_amdgcn_readlane((int)word, w + 1) : 0u;
+    const uint64_t m = ((uint64_t)hi << 32) | lo;
+    if ((m >> lane) & 1ull) col_idx[out + __popcll(m & lt_mask)] = id0 + 32 * w + lane;
+    out += __popcll(m);
+  }
+  return out;
+}
+
+// row_ptr and col_idx in one kernel when R <= kCsrMaxRows: a workgroup of
+// sixteen waves takes kCsrRows rows.  The counts of every row before them are
+// summed by the workgroup (at most kCsrMaxRows values, 16-byte loads), its
+// own rows' counts scanned by one wave; then each wave writes the kept ids
+// of four rows, their bitmask words loaded up front and the four rows walked
+// together (rows of at most 2048 blocks), or one row and one 64-word chunk
+// at a time.  Also clears the attention kernel's unit counter when it is
+// given one (the next kernel on the stream).
+constexpr int kCsrRows = 64;
+constexpr int kCsrThreads = 1024;
+constexpr int kCsrMaxRows = 32768;
+
+__global__ __launch_bounds__(kCsrThreads) void csr_build_kernel(Geom g, const int* __restrict__ counts,
+                                                                const uint32_t* __restrict__ mask, int mask_words,
+                                                                int* __restrict__ row_ptr, int* __restrict__ col_idx,
+                                                                int* __restrict__ counter) {
+  constexpr int NW = kCsrThreads / 64;   // waves
+  constexpr int RPW = kCsrRows / NW;     // rows per wave
+  __shared__ int red[NW];
+  __shared__ int start[kCsrRows];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row0 = blockIdx.x * kCsrRows;
+  const int r0 = row0 + RPW * wave;
+  // this wave's rows' bitmask words (rows of at most 2048 blocks), loaded
+  // first, every load in bounds (row and word clamped), and all retired with
+  // the loads of the counts, before any store: a wait issued after a store
+  // would also wait for the store
+  uint32_t words[RPW];
+  if (mask_words <= 64) {
+    const int lw = min(lane, mask_words - 1);
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) words[k] = mask[(size_t)min(r0 + k, g.R - 1) * mask_words + lw];
+  }
+  // rows [0, row0): row0 is a multiple of 4, counts is 16-byte aligned
+  // (two 16-byte loads in flight per thread: at most kCsrMaxRows / 8192
+  // rounds of them)
+  const int4* c4 = reinterpret_cast<const int4*>(counts);
+  const int n4 = row0 / 4;
+  int sum = 0;
+  for (int i0 = 0; i0 < n4; i0 += 2 * kCsrThreads) {
+    int4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = i0 + kCsrThreads * u + tid;
+      v[u] = i < n4 ? c4[i] : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) sum += v[u].x + v[u].y + v[u].z + v[u].w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane == 0) red[wave] = sum;
+  const int c = (tid < kCsrRows && row0 + tid < g.R) ? counts[row0 + tid] : 0;
+  __builtin_amdgcn_s_waitcnt(0);
+  if (mask_words <= 64) {
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) words[k] = (lane < mask_words && r0 + k < g.R) ? words[k] : 0u;
+  }
+  __syncthreads();
+  int end = 0;  // wave 0: row_ptr[row0 + lane + 1]
+  if (wave == 0) {
+    int base = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) base += red[w];
+    int inc = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(inc, off);
+      if (lane >= off) inc += t;
+    }
+    end = base + inc;
+    start[lane] = end - c;
+  }
+  __syncthreads();
+  // stored after the barrier, which would otherwise wait for these stores
+  if (counter != nullptr && blockIdx.x == 0 && tid == 0) *counter = 0;
+  if (wave == 0) {
+    if (row0 + lane < g.R) row_ptr[row0 + lane + 1] = end;
+    if (blockIdx.x == 0 && lane == 0) row_ptr[0] = 0;
+  }
+  if (mask_words <= 64) {
+    // for each 64 ids, the two words (made uniform with readlane) are the
+    // chunk's ballot; the rows' chains are independent
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int out[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) out[k] = start[RPW * wave + k];
+    for (int w = 0; w < mask_words; w += 2) {
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)words[k], w);
+        const uint32_t hi = w + 1 < mask_words ? (uint32_t)__builtin_amdgcn_readlane((int)words[k], w + 1) : 0u;
+        const uint64_t m = ((uint64_t)hi << 32) | lo;
+        if ((m >> lane) & 1ull) col_idx[out[k] + __popcll(m & lt_mask)] = 32 * w + lane;
+        out[k] += __popcll(m);
+      }
+    }
+  } else {
+    for (int k = 0; k < RPW && r0 + k < g.R; ++k) {
+      const uint32_t* mrow = mask + (size_t)(r0 + k) * mask_words;
+      int out = start[RPW * wave + k];
+      for (int w0 = 0; w0 < mask_words; w0 += 64) {
+        const int nw = min(64, mask_words - w0);
+        const uint32_t word = lane < nw ? mrow[w0 + lane] : 0u;
+        out = compact_row_from_lanes(word, nw, lane, out, 32 * w0, col_idx);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void compact_kernel(Geom g, const int* __restrict__ row_ptr,
                                                       const uint32_t* __restrict__ mask, int mask_words,
-                                                      int* __restrict__ col_idx) {
+                                                      int* __restrict__ col_idx, int* __restrict__ counter) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (counter != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *counter = 0;
   if (row >= g.R) return;
   const uint32_t* mrow = mask + (size_t)row * mask_words;
   int out = row_ptr[row];
@@ -721,10 +862,17 @@ hipError_t launch_scan(const Geom& g, const int* counts, int* row_ptr, int* chun
   return hipGetLastError();
 }
 
-hipError_t launch_compact(const Geom& g, const int* row_ptr, const uint32_t* mask, int mask_words,
-                          int* col_idx, hipStream_t s) {
-  if (g.R == 0) return hipSuccess;
-  compact_kernel<<<(g.R + 3) / 4, 256, 0, s>>>(g, row_ptr, mask, mask_words, col_idx);
+hipError_t launch_csr(const Geom& g, const int* counts, const uint32_t* mask, int mask_words, int* row_ptr,
+                      int* col_idx, int* chunk_sums, int* attn_counter, hipStream_t s) {
+  if (g.R == 0) return launch_scan(g, nullptr, row_ptr, nullptr, s);
+  if (g.R <= kCsrMaxRows) {
+    csr_build_kernel<<<(g.R + kCsrRows - 1) / kCsrRows, kCsrThreads, 0, s>>>(g, counts, mask, mask_words,
+                                                                              row_ptr, col_idx, attn_counter);
+    return hipGetLastError();
+  }
+  const hipError_t e = launch_scan(g, counts, row_ptr, chunk_sums, s);
+  if (e != hipSuccess) return e;
+  compact_kernel<<<(g.R + 3) / 4, 256, 0, s>>>(g, row_ptr, mask, mask_words, col_idx, attn_counter);
   return hipGetLastError();
 }
 

@@ -134,11 +134,17 @@ hipError_t launch_estimate_select(const Geom& g, const float* q_mean, const floa
 constexpr int kScanChunk = 4096;
 inline int scan_chunks(long long R) { return (int)((R + kScanChunk - 1) / kScanChunk); }
 hipError_t launch_scan(const Geom& g, const int* counts, int* row_ptr, int* chunk_sums, hipStream_t s);
-hipError_t launch_compact(const Geom& g, const int* row_ptr, const uint32_t* mask, int mask_words,
-                          int* col_idx, hipStream_t s);
+// row_ptr and col_idx from the counts and row bitmasks; chunk_sums as for
+// launch_scan.  attn_counter (may be null) is the attention kernel's unit
+// counter, cleared here for an attention launch that follows on the stream.
+hipError_t launch_csr(const Geom& g, const int* counts, const uint32_t* mask, int mask_words, int* row_ptr,
+                      int* col_idx, int* chunk_sums, int* attn_counter, hipStream_t s);
+// counter_cleared: a kernel earlier on the stream has set *counter to 0
+// (else the launch clears it first)
 hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpack, const void* vpack,
                               const int* row_ptr, const int* col_idx, long long col_capacity,
-                              float scale, void* o, int* counter, int num_cus, hipStream_t s);
+                              float scale, void* o, int* counter, bool counter_cleared, int num_cus,
+                              hipStream_t s);
 hipError_t launch_bsattn_f32(const Geom& g, const float* q, const float* k, const float* v,
                              const int* row_ptr, const int* col_idx, long long col_capacity,
                              float scale, float* o, hipStream_t s);

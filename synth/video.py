@@ -178,6 +178,14 @@ TEST_CONFIGS = {
     "dense_40": Config("dense_40", B=2, H=2, d=64, T=4, Hh=10, W=24, bt=1, bh=5, bw=8,
                        dtype="bf16", sigma=0.5, amp_kind="uniform", amp_params=(0.3, 2.0),
                        mode=MODE_MASS, budget=(0.8,), seed=26),
+    # row counts on both sides of the one-kernel CSR build's limit (32768
+    # rows): 512 and 513 heads of 64 one-token blocks.
+    "rows_32k": Config("rows_32k", B=2, H=256, d=64, T=4, Hh=4, W=4, bt=1, bh=1, bw=1,
+                       dtype="bf16", sigma=0.5, amp_kind="uniform", amp_params=(0.3, 2.0),
+                       mode=MODE_MASS, budget=(0.6,), seed=27),
+    "rows_32k_plus": Config("rows_32k_plus", B=3, H=171, d=64, T=4, Hh=4, W=4, bt=1, bh=1, bw=1,
+                            dtype="bf16", sigma=0.5, amp_kind="uniform", amp_params=(0.3, 2.0),
+                            mode=MODE_RATIO, budget=(0.3,), seed=28),
     # fp32 (debug) path on a ragged shape.
     "ragged_f32": Config("ragged_f32", B=1, H=2, d=128, T=5, Hh=7, W=9, bt=4, bh=4, bw=4,
                          dtype="f32", sigma=1.0, amp_kind="const", amp_params=(0.0,),

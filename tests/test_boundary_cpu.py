@@ -210,6 +210,33 @@ def test_compute_entry_points_reject_before_launch():
     assert e.value.status == UNSUP
 
 
+def test_misaligned_workspace_rejected_before_launch():
+    """Every entry point that takes a workspace needs it on a 256-byte
+    boundary; otherwise INVALID_ARG before anything is launched (the other
+    pointers here are stand-ins, never dereferenced)."""
+    cfg = synth.get_config("small")
+    p = _prob(cfg)
+    b = spade.Budget("ratio", [0.25] * cfg.H)
+    cap = spade.spade_max_nnz(p, b)
+    need = spade.spade_workspace_bytes(p)
+    good = [(cfg.bt, cfg.bh, cfg.bw), (1, 6, 8)]
+    n_sel = spade.spade_schemes_workspace_bytes(p, good)
+    n_att = spade.spade_schemes_workspace_bytes(p, good, b)
+    d = 0x100000  # a stand-in device address
+    for ws in (d + 16, d + 128, d + 4):
+        calls = [
+            lambda: spade.spade_estimate_select(p, d, d, b, d, d, cap, ws, need, stream=0),
+            lambda: spade.spade_block_sparse_attn(p, d, d, d, d, d, cap, d, ws, need, stream=0),
+            lambda: spade.spade_attn(p, d, d, d, b, d, d, d, cap, ws, need, stream=0),
+            lambda: spade.spade_scheme_select(p, d, d, good, d, d, ws, n_sel, stream=0),
+            lambda: spade.spade_attn_schemes(p, d, d, d, good, b, d, d, d, ws, n_att, stream=0),
+        ]
+        for call in calls:
+            with pytest.raises(spade.SpadeError) as e:
+                call()
+            assert e.value.status == INVALID, ws
+
+
 def test_empty_batch_is_a_noop():
     cfg = synth.get_config("small")
     p = _prob(cfg, B=0)

@@ -360,6 +360,41 @@ def test_limits_selection_and_attention_match_oracle(name):
     assert err <= BF16_TOL, err
 
 
+@pytest.mark.parametrize("name", ["rows_32k", "rows_32k_plus"])
+def test_csr_build_on_both_sides_of_its_row_limit(name):
+    """Up to 32768 rows the CSR (row_ptr and the ascending kept ids) comes
+    from one kernel that also clears the attention kernel's unit counter;
+    above it from the chunked scan and the per-row compaction.  Both against
+    the oracle's selection, the oracle's selection on the GPU's own scores
+    (which must reproduce the CSR exactly), and the attention on that CSR,
+    twice in a row (a counter left uncleared would skip every unit)."""
+    cfg = synth.get_config(name)
+    print(f"[csr] {name} R={cfg.B * cfg.H * 64}", flush=True)
+    x = synth.make_inputs(cfg)
+    g = geom(cfg)
+    grid, block = grid_block(cfg)
+    qd, kd = to_dev(cfg, x["q"]), to_dev(cfg, x["k"])
+    qm, km = spade.summarize(qd, kd, grid, block)
+    p = spade.problem_for(qd, grid, block)
+    scale = oracle.default_scale(cfg.d)
+    S_ref = oracle.estimate(oracle_means(cfg, x["q"]), oracle_means(cfg, x["k"]), scale)
+    sel = oracle.select(S_ref, cfg.mode, cfg.per_head_budget())
+    rp, ci = csr_rows(*spade.estimate_select(qm, km, p, cfg.mode, cfg.per_head_budget()))
+    assert compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), name) == 0
+    S_gpu = spade.debug_scores(qm, km, p).cpu().numpy()
+    sel_g = oracle.select(S_gpu, cfg.mode, cfg.per_head_budget())
+    assert np.array_equal(sel_g.row_ptr, rp)
+    assert np.array_equal(sel_g.col_idx, ci[:rp[-1]])
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    for _ in range(2):
+        o, rp2, ci2 = run_attn(cfg, x)
+        rp2, ci2 = csr_rows(rp2, ci2)
+        assert np.array_equal(rp2, rp) and np.array_equal(ci2[:rp[-1]], ci[:rp[-1]])
+        ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], g, rp, ci, scale)
+        err = np.abs(dev_to_f64(o) - ref).max()
+        assert err <= BF16_TOL, err
+
+
 @pytest.mark.parametrize("name", ["ragged_small", "ragged_p64", "tiny", "ragged_f32", "mid_full", "dense_40"])
 def test_ratio_one_equals_dense_attention(name):
     cfg = synth.get_config(name)
