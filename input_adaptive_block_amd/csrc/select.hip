@@ -285,6 +285,13 @@ __device__ inline int skip_common_bits(const uint64_t (&key)[E], int nK, int lan
     a &= cand ? key[e] : ~0ull;
   }
   wave_or_and(o, a);
+  // every lane holds the same words: read them into scalar registers, so the
+  // bit the search resumes at is wave-uniform and the search loop stays a
+  // scalar loop
+  o = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(o >> 32)) << 32) |
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)o);
+  a = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32) |
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   const uint64_t diff = (o ^ a) & low;
   if (diff == 0ull) {
     T = (T & ~low) | (o & low);
@@ -348,7 +355,9 @@ __device__ inline void select_row(const Geom& g, const SelectArgs& a, int row, i
       p[e] = (64 * e + lane < nK) ? exp_nonpos(key_score(key[e]) - mx) : 0.0;
       loc += p[e];
     }
-    const double Z = wave_sum(loc);
+    // (every lane holds the same sum: read into scalar registers, so the
+    // target and the search's control flow below are wave-uniform)
+    const double Z = read_lane_f64(wave_sum(loc), 0);
     const double target = a.tau[h] * Z;
     // largest T with mass(key >= T) >= target; mass(key >= T) is monotone
     // non-increasing in T because every partial sum only drops non-negative
@@ -363,10 +372,14 @@ __device__ inline void select_row(const Geom& g, const SelectArgs& a, int row, i
     bool tested = false;
     for (; bit >= 0; --bit) {
       const uint64_t cand = T | (1ull << bit);
-      double f = 0.0;
+      double f0 = 0.0, f1 = 0.0;  // two chains of adds instead of one
 #pragma unroll
-      for (int e = 0; e < E; ++e) f += (key[e] >= cand) ? p[e] : 0.0;
-      if (wave_sum(f) >= target) T = cand;
+      for (int e = 0; e < E; e += 2) {
+        f0 += (key[e] >= cand) ? p[e] : 0.0;
+        if (e + 1 < E) f1 += (key[e + 1] >= cand) ? p[e + 1] : 0.0;
+      }
+      // every lane holds the same sum: the ballot makes the test wave-uniform
+      if (__builtin_amdgcn_ballot_w64(wave_sum(f0 + f1) >= target) != 0ull) T = cand;
       if (skip && !tested && bit > 0) {
         tested = true;
         bit = skip_common_bits(key, nK, lane, T, bit - 1) + 1;  // the loop steps to the returned bit
