@@ -145,51 +145,64 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
       uint16_t* pk = nullptr;
       if (PACK) pk = (role == 0 ? qpack : kpack) + ((size_t)bh * g.nblk + j) * (size_t)g.P * D;
       const int rows = PACK ? g.P : box.n;
-      for (int l = lrow; l < rows; l += TPP) {
-        Vec16 x = {{0u, 0u, 0u, 0u}};
-        if (l < box.n) {
-          const int tok = block_token(g, box, l);
-          x = *reinterpret_cast<const Vec16*>(src + (head_base + (size_t)tok * D + c0) * elem);
-        }
-        if (want_mean || want_sics) {
-          double xe[EPV];
-          if (BF16) {
+      // the token rows of NB passes are loaded before any of them is used
+      constexpr int NB = 4;
+      for (int l0 = lrow; l0 < rows; l0 += NB * TPP) {
+        Vec16 xs[NB];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              xe[2 * e] = (double)bf16_lo(x.w[e]);
-              xe[2 * e + 1] = (double)bf16_hi(x.w[e]);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) xe[e] = (double)__uint_as_float(x.w[e]);
-          }
-          if (MEAN && l < box.n) {  // padded rows (zeros) take no part in a max or min
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) acc[e] = sum_op_t<OP>(acc[e], xe[e]);
-          }
-          if (want_sics) {
-            // squared norm of the token over its TPT threads (consecutive lanes;
-            // every thread of the group runs the same iterations)
-            double ss = 0.0;
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) ss += xe[e] * xe[e];
-            ss = group_sum<TPT>(ss);
-            // 1/|x|: fp32 reciprocal square root refined by one Newton step in
-            // fp64 (relative error ~1e-14, far below the fp32 result's ulp)
-            double inv = 0.0;
-            if (ss > 0.0) {
-              const double r = (double)__builtin_amdgcn_rsqf((float)ss);
-              inv = r * (1.5 - 0.5 * ss * r * r);
-            }
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) uacc[e] += xe[e] * inv;
+        for (int b = 0; b < NB; ++b) {
+          const int l = l0 + b * TPP;
+          xs[b] = Vec16{{0u, 0u, 0u, 0u}};
+          if (l < box.n) {
+            const int tok = block_token(g, box, l);
+            xs[b] = *reinterpret_cast<const Vec16*>(src + (head_base + (size_t)tok * D + c0) * elem);
           }
         }
-        if (PACK) {
-          const int sub = l >> 5, kl = l & 31;
-          const int c = c0 >> 4, half = (c0 >> 3) & 1;
-          const size_t dst = ((size_t)(sub * (D / 16) + c) * 64 + kl + 32 * half) * 8;
-          *reinterpret_cast<Vec16*>(pk + dst) = x;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int l = l0 + b * TPP;
+          if (l >= rows) break;
+          const Vec16 x = xs[b];
+          if (want_mean || want_sics) {
+            double xe[EPV];
+            if (BF16) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                xe[2 * e] = (double)bf16_lo(x.w[e]);
+                xe[2 * e + 1] = (double)bf16_hi(x.w[e]);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) xe[e] = (double)__uint_as_float(x.w[e]);
+            }
+            if (MEAN && l < box.n) {  // padded rows (zeros) take no part in a max or min
+#pragma unroll
+              for (int e = 0; e < EPV; ++e) acc[e] = sum_op_t<OP>(acc[e], xe[e]);
+            }
+            if (want_sics) {
+              // squared norm of the token over its TPT threads (consecutive lanes;
+              // every thread of the group runs the same iterations)
+              double ss = 0.0;
+#pragma unroll
+              for (int e = 0; e < EPV; ++e) ss += xe[e] * xe[e];
+              ss = group_sum<TPT>(ss);
+              // 1/|x|: fp32 reciprocal square root refined by one Newton step in
+              // fp64 (relative error ~1e-14, far below the fp32 result's ulp)
+              double inv = 0.0;
+              if (ss > 0.0) {
+                const double r = (double)__builtin_amdgcn_rsqf((float)ss);
+                inv = r * (1.5 - 0.5 * ss * r * r);
+              }
+#pragma unroll
+              for (int e = 0; e < EPV; ++e) uacc[e] += xe[e] * inv;
+            }
+          }
+          if (PACK) {
+            const int sub = l >> 5, kl = l & 31;
+            const int c = c0 >> 4, half = (c0 >> 3) & 1;
+            const size_t dst = ((size_t)(sub * (D / 16) + c) * 64 + kl + 32 * half) * 8;
+            *reinterpret_cast<Vec16*>(pk + dst) = x;
+          }
         }
       }
     };
@@ -201,16 +214,26 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
     uint16_t* pk = vpack + ((size_t)bh * g.nblk + j) * (size_t)g.P * D;
     for (int base = 0; base < g.P; base += 128) {
       const int nrows = min(128, g.P - base);
-      for (int l = lrow; l < nrows; l += TPP) {
-        Vec16 x = {{0u, 0u, 0u, 0u}};
-        const int lt = base + l;
-        if (lt < box.n) {
-          const int tok = block_token(g, box, lt);
-          x = *reinterpret_cast<const Vec16*>(src + (head_base + (size_t)tok * D + c0) * elem);
-        }
-        uint32_t* row = reinterpret_cast<uint32_t*>(&vt[l * VROW + c0]);
+      constexpr int NB = 4;
+      for (int l0 = lrow; l0 < nrows; l0 += NB * TPP) {
+        Vec16 xs[NB];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) row[e] = x.w[e];
+        for (int b = 0; b < NB; ++b) {
+          const int lt = base + l0 + b * TPP;
+          xs[b] = Vec16{{0u, 0u, 0u, 0u}};
+          if (l0 + b * TPP < nrows && lt < box.n) {
+            const int tok = block_token(g, box, lt);
+            xs[b] = *reinterpret_cast<const Vec16*>(src + (head_base + (size_t)tok * D + c0) * elem);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int l = l0 + b * TPP;
+          if (l >= nrows) break;
+          uint32_t* row = reinterpret_cast<uint32_t*>(&vt[l * VROW + c0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) row[e] = xs[b].w[e];
+        }
       }
       __syncthreads();
       // output vectors of this chunk: (sub, m, kc, lane) -> 8 keys at one channel
