@@ -487,6 +487,69 @@ def test_zero_queries_select_lowest_ids():
             assert ci[rp[r]:rp[r + 1]].tolist() == list(range(k))
 
 
+@pytest.mark.parametrize("grid", [(4, 4, 4), (8, 8, 8), (8, 8, 10)])
+def test_mass_targets_on_a_whole_number_of_blocks(grid):
+    """Zero query summaries make every score 0 and every weight exactly 1, so
+    all mass sums are exact integers and every key ties.  With tau * nblk
+    exactly an integer m the mass of the top m blocks equals the target
+    (kept: the m lowest ids); one fp32 step of tau above, m + 1; one step
+    below, m (rows of 64, 512 and 640 blocks: 1, 8 and 10 keys per lane)."""
+    nblk = grid[0] * grid[1] * grid[2]
+    B, H, d = 1, 3, 64
+    q = torch.zeros(B, H, nblk, d, dtype=torch.bfloat16, device="cuda")
+    p = spade.problem_for(q, grid, (1, 1, 1))
+    assert spade.spade_num_blocks(p) == nblk
+    qm = torch.zeros(B, H, nblk, d, dtype=torch.float32, device="cuda")
+    km = torch.from_numpy(np.random.default_rng(11).standard_normal((B, H, nblk, d)).astype(np.float32)).cuda()
+    m = 5 * (nblk // 40) + 5  # m / nblk is a dyadic fraction: exact in fp32
+    t = np.float32(m) / np.float32(nblk)
+    assert float(t) * nblk == m
+    taus = [t, np.nextafter(t, np.float32(1)), np.nextafter(t, np.float32(0))]
+    want = [m, m + 1, m]
+    for tau, k in zip(taus, want):
+        rp, ci = csr_rows(*spade.estimate_select(qm, km, p, "mass", [float(tau)] * H))
+        assert rp[-1] == k * B * H * nblk, (tau, k)
+        for r in range(len(rp) - 1):
+            assert ci[rp[r]:rp[r + 1]].tolist() == list(range(k)), (tau, r)
+
+
+@pytest.mark.parametrize("grid", [(4, 4, 4), (8, 8, 8), (8, 8, 10)])
+def test_mass_target_next_to_the_mass_of_the_top_blocks(grid):
+    """Five blocks score 0 (weight exactly 1), the others score below -1, all
+    distinct; tau is the fp32 value nearest 5 / Z and its two fp32 neighbours,
+    so the mass of the five top blocks (the first test of each search splits
+    them from the rest) lies within a few 1e-7 of the target, on either side:
+    five or six blocks kept.  Every row against the oracle's selection, with
+    no row allowed to differ: the targets sit 1e-8 to 5e-7 from that mass,
+    far beyond the two sides' differences in Z (about 1e-16 relative)."""
+    nblk = grid[0] * grid[1] * grid[2]
+    B, H, d = 1, 2, 64
+    q = torch.zeros(B, H, nblk, d, dtype=torch.bfloat16, device="cuda")
+    p = spade.problem_for(q, grid, (1, 1, 1))
+    scale = oracle.default_scale(d)
+    qm = np.zeros((B, H, nblk, d), np.float32)
+    qm[..., 0] = 1.0
+    km = np.zeros((B, H, nblk, d), np.float32)
+    svals = -1.0 - 0.01 * np.arange(nblk - 5) - 0.001 * np.arange(H)[:, None]
+    km[0, :, 5:, 0] = (svals / scale).astype(np.float32)
+    S_ref = oracle.estimate(qm.astype(np.float64), km.astype(np.float64), scale)
+    Z = np.exp(S_ref[0, :, 0, :] - S_ref[0, :, 0, :].max(axis=1, keepdims=True)).sum(axis=1)
+    qd, kd = torch.from_numpy(qm).cuda(), torch.from_numpy(km).cuda()
+    for step in (0, 1, -1):
+        taus = []
+        for h in range(H):
+            t = np.float32(5.0 / Z[h])
+            if step:
+                t = np.nextafter(t, np.float32(1.0 if step > 0 else 0.0))
+            assert abs(float(t) * Z[h] - 5.0) < 1e-6 * Z[h]
+            taus.append(float(t))
+        sel = oracle.select(S_ref, "mass", taus)
+        rp, ci = csr_rows(*spade.estimate_select(qd, kd, p, "mass", taus))
+        assert compare_selection(sel, rp, ci, S_ref, "mass", taus, f"{grid} step {step}") == 0
+        kept = sel.counts.reshape(H, nblk)[:, 0]
+        assert set(kept.tolist()) <= {5, 6}
+
+
 def test_deterministic_and_writes_every_output_once():
     cfg = synth.get_config("mid_shape")
     x = synth.make_inputs(cfg)
