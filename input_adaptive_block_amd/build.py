@@ -64,6 +64,46 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     return lib
 
 
+def kernel_resources() -> dict:
+    """Per-kernel register and memory figures of the device code, read from
+    the code-object metadata of a device-only assembly build of every HIP
+    source: {kernel symbol: {"vgpr": n, "vgpr_spill": n, "sgpr_spill": n,
+    "scratch": bytes of private (scratch) memory per lane}}."""
+    import re
+    asm_dir = os.path.join(BUILD, "asm")
+    os.makedirs(asm_dir, exist_ok=True)
+
+    def one(src: str) -> str:
+        out = os.path.join(asm_dir, src + ".s")
+        cmd = [HIPCC, *[f for f in FLAGS if f != "-fPIC"], "--cuda-device-only", "-S",
+               os.path.join(CSRC, src), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stderr}")
+        return out
+
+    hips = [f for f in SOURCES if f.endswith(".hip")]
+    with ThreadPoolExecutor(max_workers=len(hips)) as ex:
+        outs = list(ex.map(one, hips))
+    res = {}
+    for out in outs:
+        text = open(out).read()
+        # the metadata block of each kernel: ".name: <symbol>" then its fields
+        for m in re.finditer(r"\.name:\s+(\S+)\n((?:\s+\.[a-z_]+:.*\n)+)", text):
+            body = m.group(2)
+
+            def field(k):
+                f = re.search(r"\." + k + r":\s+(\d+)", body)
+                return int(f.group(1)) if f else None
+
+            if field("vgpr_count") is None:
+                continue
+            res[m.group(1)] = {"vgpr": field("vgpr_count"), "vgpr_spill": field("vgpr_spill_count"),
+                               "sgpr_spill": field("sgpr_spill_count"),
+                               "scratch": field("private_segment_fixed_size")}
+    return res
+
+
 if __name__ == "__main__":
     build(verbose=True, sanitize="--sanitize" in sys.argv)
     sys.exit(0)

@@ -372,3 +372,27 @@ def test_attention_walk_by_block_shape(name, dense):
     cfg = synth.get_config(name)
     assert spade.spade_debug_dense_walk(_prob(cfg)) == dense
     assert spade.spade_debug_dense_walk(_prob(cfg, dtype=spade.SPADE_F32)) == 0
+
+
+def test_device_code_fits_its_registers_without_scratch():
+    """Every kernel of the library runs without scratch (private) memory and
+    without register spills, so no launch makes the runtime set scratch
+    aside (the allocation-free entry point relies on that), and the kernels
+    that depend on their occupancy fit it: the attention kernel's twelve
+    waves per CU (three per SIMD: at most 168 registers) and the fused
+    selection kernel's four waves per SIMD (at most 128)."""
+    if not os.path.exists(os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")):
+        pytest.skip("no hipcc")
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_spade_build", os.path.join(ROOT, "input_adaptive_block_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    res = mod.kernel_resources()
+    assert len(res) >= 40
+    for name, r in res.items():
+        assert r["scratch"] == 0 and r["vgpr_spill"] == 0, (name, r)
+        if "bsattn_bf16_kernel" in name:
+            assert r["vgpr"] <= 168, (name, r)
+        if "estimate_select_kernel" in name and ("ELi12EE" not in name and "ELi16EE" not in name):
+            assert r["vgpr"] <= 128, (name, r)
