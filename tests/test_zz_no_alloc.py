@@ -4,7 +4,8 @@ scratch) against the workspace entry point, through the C ABI.
 Both run the same kernels, so the CSRs must be identical (index work:
 bit-exact).  The calls come in a row on one device, each one smaller than the
 one before, so a call that relied on the buffer's earlier contents would show
-up as a difference."""
+up as a difference.  The first two sit on both sides of the row count where
+the CSR moves from one kernel to the chunked scan."""
 import numpy as np
 import pytest
 
@@ -44,6 +45,8 @@ def _same_csr(a, b):
 
 # (config, budget mode or None for the config's own, per-head value, window)
 CALLS = [
+    ("rows_32k_plus", None, None, None),            # 32,832 rows: the chunked scan's chunk sums in the buffer
+    ("rows_32k", None, None, None),                 # 32,768 rows: the one-kernel CSR's limit
     ("mid", None, None, None),                      # 25,200 rows, mass 0.9
     ("small", None, None, None),                    # 5,460 rows, ratio 0.25
     ("mid_shape", "count", 3, (1, 1, 1)),           # 24 rows, top-3 united with a window
