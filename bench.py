@@ -344,6 +344,9 @@ def main():
             "attention_kernel": attn_avg,
             "attention_kernel_again": attn_same_ms,
             "attention_kernel_zero_qkv": attn_zero_ms,
+            # diagnostic only: the same kept pairs' FLOPs over the zero-data time
+            # (the clock the part holds when nothing toggles), not the metric
+            "attention_kernel_zero_qkv_frac_bf16_peak": flops / (attn_zero_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "non_attention_share_of_step": 1.0 - attn_avg / ms_per_step,
         },
         "roofline": {
