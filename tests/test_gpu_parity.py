@@ -868,6 +868,17 @@ def test_full_size_attn_schemes_ragged():
         check_rows(cc, x, oc, rp_h, ci_h, sorted(rows), BF16_TOL, f"{cfg.name} candidate {blk}")
 
 
+def f32_logit_bound(xf, scale):
+    """(L, bound) for the fp32 path: L = scale max|q| max|k| bounds every
+    logit, and fp32 rounding of a d-term dot product moves a logit by at most
+    about sqrt(d) 2^-24 L, so the output moves by at most 8 sqrt(d) 2^-24 L
+    max|v| (the factor 8 covers the max subtraction, the exponential and the
+    normalisation)."""
+    d = xf["q"].shape[-1]
+    L = scale * np.linalg.norm(xf["q"], axis=-1).max() * np.linalg.norm(xf["k"], axis=-1).max()
+    return L, 8 * math.sqrt(d) * 2.0 ** -24 * L * np.abs(xf["v"]).max()
+
+
 def test_f32_debug_path_with_large_logits():
     """The fp32 debug path on the mid block shape with hot blocks (+3 on every
     channel of some blocks): logits reach about 110, where fp32 rounding of
@@ -888,10 +899,7 @@ def test_f32_debug_path_with_large_logits():
     assert compare_selection(sel, rp, ci, S_ref, cfg.mode, cfg.per_head_budget(), cfg.name) == 0
     ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], g, rp, ci, scale)
     err = float(np.abs(dev_to_f64(o) - ref).max())
-    nq = np.linalg.norm(xf["q"], axis=-1).max()
-    nk = np.linalg.norm(xf["k"], axis=-1).max()
-    L = scale * nq * nk
-    bound = 8 * math.sqrt(cfg.d) * 2.0 ** -24 * L * np.abs(xf["v"]).max()
+    L, bound = f32_logit_bound(xf, scale)
     print(f"[f32 large logits] max logit bound {L:.1f}, max-abs error {err:.3e}, bound {bound:.3e}", flush=True)
     assert err <= max(F32_TOL, bound)
 
@@ -950,3 +958,76 @@ def test_whole_path_in_a_hip_graph(name):
         # eager work between replays
         spade.attn(q, k, v, grid, block, cfg.mode, cfg.per_head_budget())
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# seeded random problems: shapes, ragged tails, head dims, budgets, windows
+# and summarizers drawn together, so that combinations no named case lists
+# still meet the oracle
+# ---------------------------------------------------------------------------
+
+def random_case(seed):
+    """A small seeded problem: every grid axis gets a ragged tail with
+    probability 2/3, block tokens up to 512, at most 4 (batch, head) pairs and
+    6,000 tokens, so the oracle finishes in a second or two."""
+    r = np.random.Generator(np.random.PCG64([seed, 71]))
+    bt, bh, bw = int(r.integers(1, 5)), int(r.integers(1, 9)), int(r.integers(1, 17))
+    while True:
+        ext = [b * int(r.integers(1, 7)) + (int(r.integers(0, b)) if r.random() < 2 / 3 else 0)
+               for b in (bt, bh, bw)]
+        if all(e > 0 for e in ext) and ext[0] * ext[1] * ext[2] <= 6000:
+            break
+    T, Hh, W = ext
+    B, H = [(1, 1), (1, 2), (2, 1), (2, 2), (1, 4)][int(r.integers(0, 5))]
+    d = (64, 128)[int(r.integers(0, 2))]
+    dtype = "f32" if r.random() < 0.2 else "bf16"
+    cfg = synth.Config(f"random{seed}", B=B, H=H, d=d, T=T, Hh=Hh, W=W, bt=bt, bh=bh, bw=bw,
+                       dtype=dtype, sigma=float(r.uniform(0.2, 1.0)), amp_kind="uniform",
+                       amp_params=(0.2, 2.5), mode="count", budget=(1,), seed=1000 + seed)
+    nblk = cfg.nblk
+    mode = ("count", "ratio", "mass")[int(r.integers(0, 3))]
+    window = None
+    if r.random() < 0.4:
+        window = tuple(int(x) for x in r.integers(0, 3, size=3))
+    lo = 0 if window is not None and r.random() < 0.3 else 1
+    if mode == "count":
+        budget = [float(r.integers(lo, nblk + 1)) for _ in range(H)]
+    elif mode == "ratio":
+        budget = [0.0 if lo == 0 and r.random() < 0.5 else float(r.uniform(0.02, 1.0)) for _ in range(H)]
+    else:
+        budget = [0.0 if lo == 0 and r.random() < 0.5 else float(r.uniform(0.05, 0.999)) for _ in range(H)]
+    summarizer = ("mean", "mean", "max", "min")[int(r.integers(0, 4))]
+    return cfg, mode, budget, window, summarizer
+
+
+RANDOM_SEEDS = list(range(48))
+
+
+@pytest.mark.parametrize("seed", RANDOM_SEEDS)
+def test_random_problems_match_oracle(seed):
+    cfg, mode, budget, window, summarizer = random_case(seed)
+    label = (f"seed {seed}: B{cfg.B} H{cfg.H} d{cfg.d} {cfg.dtype} grid {cfg.T}x{cfg.Hh}x{cfg.W} "
+             f"block {cfg.bt}x{cfg.bh}x{cfg.bw} {mode} {budget} window {window} {summarizer}")
+    print(label, flush=True)
+    x = synth.make_inputs(cfg)
+    g = geom(cfg)
+    grid, block = grid_block(cfg)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    o, rp, ci = spade.attn(q, k, v, grid, block, mode, budget, summarizer=summarizer, window=window)
+    torch.cuda.synchronize()
+    rp, ci = csr_rows(rp, ci)
+    scale = oracle.default_scale(cfg.d)
+    if summarizer == "mean":
+        qs, ks = oracle_means(cfg, x["q"]), oracle_means(cfg, x["k"])
+    else:
+        qs, ks = oracle_summaries(cfg, x["q"], summarizer), oracle_summaries(cfg, x["k"], summarizer)
+    S_ref = oracle.estimate(qs, ks, scale)
+    sel = oracle.select(S_ref, mode, budget, window=window, g=g)
+    assert compare_selection(sel, rp, ci, S_ref, mode, budget, label) == 0, label
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], g, rp, ci, scale)
+    # fp32: 1e-5, or the rounding bound of the dot products where the drawn
+    # amplitudes make logits large
+    tol = BF16_TOL if cfg.dtype == "bf16" else max(F32_TOL, f32_logit_bound(xf, scale)[1])
+    err = np.abs(dev_to_f64(o) - ref).max()
+    assert err <= tol, f"{label}: max error {err} (bar {tol:.2e})"
