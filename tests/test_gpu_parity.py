@@ -1031,3 +1031,73 @@ def test_random_problems_match_oracle(seed):
     tol = BF16_TOL if cfg.dtype == "bf16" else max(F32_TOL, f32_logit_bound(xf, scale)[1])
     err = np.abs(dev_to_f64(o) - ref).max()
     assert err <= tol, f"{label}: max error {err} (bar {tol:.2e})"
+
+
+def random_candidates(r, cfg, n):
+    """n further blocking candidates for the grid of cfg: distinct shapes of at
+    most 512 tokens, each axis at most the grid's extent; first those with the
+    layer block's token count (whose aggregates differ only by the shape, so
+    that heads may choose differently), then any."""
+    lim = (min(cfg.T, 8), min(cfg.Hh, 8), min(cfg.W, 16))
+    n0 = cfg.bt * cfg.bh * cfg.bw
+    same = [(a, b, n0 // (a * b)) for a in range(1, lim[0] + 1) for b in range(1, lim[1] + 1)
+            if n0 % (a * b) == 0 and n0 // (a * b) <= lim[2] and (a, b, n0 // (a * b)) != (cfg.bt, cfg.bh, cfg.bw)]
+    out = [same[i] for i in r.permutation(len(same))[:n]]
+    while len(out) < n:
+        blk = (int(r.integers(1, min(cfg.T, 8) + 1)), int(r.integers(1, min(cfg.Hh, 8) + 1)),
+               int(r.integers(1, min(cfg.W, 16) + 1)))
+        if blk[0] * blk[1] * blk[2] <= 512 and blk != (cfg.bt, cfg.bh, cfg.bw) and blk not in out:
+            out.append(blk)
+    return out
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_random_head_wise_schemes(seed):
+    """Head-wise schemes on seeded random problems with two to four blocking
+    candidates: the choice against the oracle's aggregates, every head bit for
+    bit the single-scheme run with the blocking it chose, and each of those
+    runs against the oracle (selection row by row, outputs on its CSR)."""
+    cfg, mode, budget, window, summarizer = random_case(100 + seed)
+    # heads of pure noise next to heads of structured tokens, so that heads
+    # can choose different blockings
+    cfg = dataclasses.replace(cfg, amp_kind="split", amp_params=(max(1, cfg.H // 2), 0.0, 2.5))
+    r = np.random.Generator(np.random.PCG64([seed, 72]))
+    cands = [(cfg.bt, cfg.bh, cfg.bw)] + random_candidates(r, cfg, int(r.integers(1, 4)))
+    geoms = [oracle.Geometry(cfg.T, cfg.Hh, cfg.W, *blk) for blk in cands]
+    if mode == "count":
+        budget = [min(b, min(gc.nblk for gc in geoms)) for b in budget]
+    label = (f"seed {seed}: B{cfg.B} H{cfg.H} d{cfg.d} {cfg.dtype} grid {cfg.T}x{cfg.Hh}x{cfg.W} "
+             f"candidates {cands} {mode} {budget} window {window} {summarizer}")
+    print(label, flush=True)
+    x = synth.make_inputs(cfg)
+    grid = (cfg.T, cfg.Hh, cfg.W)
+    q, k, v = (to_dev(cfg, x[n]) for n in ("q", "k", "v"))
+    o, scheme, agg = spade.attn_schemes(q, k, v, grid, cands, mode, budget, summarizer=summarizer, window=window)
+    torch.cuda.synchronize()
+    sch = scheme.cpu().numpy()
+    xf = {n: to_f64(cfg, x[n]) for n in ("q", "k", "v")}
+    ref_agg = oracle.scheme_aggregate(xf["q"], xf["k"], cfg.T, cfg.Hh, cfg.W, cands)
+    np.testing.assert_allclose(agg.cpu().numpy().astype(np.float64), ref_agg, rtol=1e-6, atol=1e-9)
+    choice, margin = oracle.choose_scheme(ref_agg)
+    assert ((sch == choice) | (margin <= 1e-9)).all(), label
+    scale = oracle.default_scale(cfg.d)
+    tol = BF16_TOL if cfg.dtype == "bf16" else max(F32_TOL, f32_logit_bound(xf, scale)[1])
+    for c, (blk, gc) in enumerate(zip(cands, geoms)):
+        if not (sch == c).any():
+            continue
+        oc, rp, ci = spade.attn(q, k, v, grid, blk, mode, budget, summarizer=summarizer, window=window)
+        torch.cuda.synchronize()
+        m = torch.from_numpy(sch == c).cuda()
+        assert torch.equal(o[m], oc[m]), f"{label}: heads of candidate {c}"
+        rp, ci = csr_rows(rp, ci)
+        qs = np.empty((cfg.B, cfg.H, gc.nblk, cfg.d))
+        ks = np.empty_like(qs)
+        for h in range(cfg.H):
+            qs[:, h:h + 1] = oracle.summarize(xf["q"][:, h:h + 1], gc, op=summarizer)
+            ks[:, h:h + 1] = oracle.summarize(xf["k"][:, h:h + 1], gc, op=summarizer)
+        S_ref = oracle.estimate(qs, ks, scale)
+        sel = oracle.select(S_ref, mode, budget, window=window, g=gc)
+        assert compare_selection(sel, rp, ci, S_ref, mode, budget, f"{label} / {blk}") == 0
+        ref = oracle.attention_full(xf["q"], xf["k"], xf["v"], gc, rp, ci, scale)
+        err = np.abs(dev_to_f64(oc) - ref).max()
+        assert err <= tol, f"{label} / {blk}: max error {err}"
