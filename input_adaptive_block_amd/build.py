@@ -104,6 +104,43 @@ def kernel_resources() -> dict:
     return res
 
 
+def first_mfma_offsets(src: str = "bsattn.hip") -> dict:
+    """Byte offset of the first MFMA instruction from the entry of each kernel
+    of src, in a device-only build of it (the disassembly of the code object
+    built here): {kernel symbol: offset}.  Kernel entries are 256-byte aligned,
+    so the offset fixes where the kernel's loops sit relative to the
+    instruction fetch boundaries."""
+    import re
+    llvm = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "llvm", "bin")
+    out_dir = os.path.join(BUILD, "codeobj")
+    os.makedirs(out_dir, exist_ok=True)
+    obj = os.path.join(out_dir, src + ".o")
+    co = os.path.join(out_dir, src + ".gfx950.co")
+    cmd = [HIPCC, *[f for f in FLAGS if f != "-fPIC"], "--cuda-device-only", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stderr}")
+    cmd = [os.path.join(llvm, "clang-offload-bundler"), "--unbundle", "--type=o", "--input=" + obj,
+           "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", "--output=" + co]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"unbundling failed:\n{' '.join(cmd)}\n{r.stderr}")
+    r = subprocess.run([os.path.join(llvm, "llvm-objdump"), "-d", co], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"llvm-objdump failed:\n{r.stderr}")
+    res, cur = {}, None
+    for line in r.stdout.splitlines():
+        m = re.match(r"^([0-9a-f]+) <(\S+)>:", line)
+        if m:
+            cur = (int(m.group(1), 16), m.group(2))
+            continue
+        if cur and cur[1] not in res and "v_mfma" in line:
+            a = re.search(r"// ([0-9A-F]+):", line)
+            if a:
+                res[cur[1]] = int(a.group(1), 16) - cur[0]
+    return res
+
+
 if __name__ == "__main__":
     build(verbose=True, sanitize="--sanitize" in sys.argv)
     sys.exit(0)

@@ -15,7 +15,9 @@
 //   each wavefront computes only on the blocks its own row keeps.  A K/V byte
 //   fetched once serves every row of the unit that keeps its block, which
 //   cuts L2 / Infinity-Cache traffic on video layers, where neighbouring rows
-//   keep mostly the same blocks.
+//   keep mostly the same blocks.  When the units would leave a last round
+//   less than half full (a small layer has only a few units per CU), that
+//   round's units go out as twice as many halves of six items each.
 // * One persistent workgroup of 12 wavefronts per CU (three per SIMD) takes
 //   units from one atomic counter in (head, row) order, so the units in
 //   flight across the chip read the K/V of one or two heads, which stay in the
@@ -205,7 +207,7 @@ template <int D, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     Geom g, const uint16_t* __restrict__ qpack, const uint16_t* __restrict__ kpack,
     const uint16_t* __restrict__ vpack, const int* __restrict__ row_ptr, const int* __restrict__ col_idx,
-    long long cap, float scale_log2, uint16_t* __restrict__ out, int* __restrict__ counter, int U) {
+    long long cap, float scale_log2, uint16_t* __restrict__ out, int* __restrict__ counter, int U, int Ufull) {
   constexpr int SUB = 32 * D;                  // bf16 elements of one 32-key subtile
   constexpr int STAGE_KB = 2 * SUB * 2 / 1024;  // 1 KB copies per tensor per stage (2 subtiles)
   constexpr int CPW = STAGE_KB / kCopyWaves;   // copies per copying wave per tensor
@@ -240,19 +242,30 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
     __syncthreads();
     const int unit = s_unit;
     if (unit < 0) break;
+    // Code placement: these no-ops put the stage loop's code 16 bytes past a
+    // 32-byte boundary (the first MFMA of the d = 128 kernel), the phase at
+    // which that loop measures about 1 % faster than at the other 8-byte
+    // phases; a host test checks the offset in the built code object.
+    asm volatile("s_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0");
 
-    const int bh = unit / um.per_head;
-    const int pi = unit - bh * um.per_head;
+    // ids from Ufull on are halves of the last units, six items each (waves
+    // 6 .. 11 idle): a last round that would keep only a few CUs busy is
+    // spread over twice as many, each walking the smaller union of its rows
+    const int whole = unit < Ufull ? unit : Ufull + ((unit - Ufull) >> 1);
+    const int nit = unit < Ufull ? kWaves : kWaves / 2;  // items of this unit
+    const int bh = whole / um.per_head;
+    const int pi = whole - bh * um.per_head;
     const size_t head_off = (size_t)bh * g.nblk * (size_t)g.P * D;
-    if (!head_active(g, bh)) {
-      // another scheme's head: nothing to compute or write; s_unit is reused
+    const int it0 = kWaves * pi + (unit >= Ufull && ((unit - Ufull) & 1) ? kWaves / 2 : 0);
+    if (!head_active(g, bh) || it0 >= um.items) {
+      // another scheme's head, or the empty second half of a head's last
+      // unit: nothing to compute or write; s_unit is reused
       __syncthreads();
       continue;
     }
 
     // ---- the unit's union list of kept blocks, with row masks ----
-    const int it0 = kWaves * pi;
-    const int it_last = min(um.items, it0 + kWaves) - 1;
+    const int it_last = min(um.items, it0 + nit) - 1;
     const int row0 = it0 / um.nsub;
     const int nrows = it_last / um.nsub - row0 + 1;  // 1 .. kMaxUnitRows
     for (int t = tid; t < (g.nblk + 1) / 2; t += kThreads) rowbits[t] = 0u;
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void bsattn_bf16_kernel(
 
     // ---- this wave's 32 queries ----
     const int my_it = it0 + wave;
-    const bool has_item = my_it < um.items;
+    const bool has_item = wave < nit && my_it < um.items;
     const int my_i = has_item ? my_it / um.nsub : row0;
     const int qsub = has_item ? my_it - my_i * um.nsub : 0;
     const int my_row = my_i - row0;  // this wave's bit in the union masks
@@ -768,14 +781,23 @@ hipError_t launch_bsattn_bf16(const Geom& g, const void* qpack, const void* kpac
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // When the units would leave a last round less than half full (as for a
+  // small layer of a few units per CU), the last round's units go out as
+  // twice as many half units: Ufull whole units, then 2 (U - Ufull) halves.
+  int Ufull = U;
+  if (num_cus > 0) {
+    const int rem = U % num_cus;
+    if (rem > 0 && 2 * rem <= num_cus) Ufull = U - rem;
+  }
+  const int ids = Ufull + 2 * (U - Ufull);
   int grid = num_cus;  // one 12-wave workgroup per CU (LDS-limited)
-  if (grid > U) grid = U;
+  if (grid > ids) grid = ids;
   if (grid < 1) grid = 1;
   const float scale_log2 = scale * 1.4426950408889634f;
 #define SPADE_BSATTN(DD, DN)                                                                                  \
   bsattn_bf16_kernel<DD, DN><<<grid, kThreads, 0, s>>>(g, (const uint16_t*)qpack, (const uint16_t*)kpack,           \
                                                      (const uint16_t*)vpack, row_ptr, col_idx, col_capacity,      \
-                                                     scale_log2, (uint16_t*)o, counter, U)
+                                                     scale_log2, (uint16_t*)o, counter, ids, Ufull)
   if (g.d == 128) {
     if (g.dense) SPADE_BSATTN(128, true);
     else SPADE_BSATTN(128, false);

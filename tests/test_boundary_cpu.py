@@ -396,3 +396,22 @@ def test_device_code_fits_its_registers_without_scratch():
             assert r["vgpr"] <= 168, (name, r)
         if "estimate_select_kernel" in name and ("ELi12EE" not in name and "ELi16EE" not in name):
             assert r["vgpr"] <= 128, (name, r)
+
+
+def test_attention_stage_loop_code_phase():
+    """The d = 128 attention kernel's stage loop sits 16 bytes past a 32-byte
+    boundary of its code (first MFMA offset = 16 mod 32): at the other 8-byte
+    phases the loop measured 1 % slower (Mid: 57.5 ms at phases 16 and 48 of
+    64, 58.0-58.5 ms at 0, 8, 24 and 56).  A change to the code before the loop
+    moves it; the no-ops at the start of each unit then need retuning."""
+    if not os.path.exists(os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")):
+        pytest.skip("no hipcc")
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_spade_build", os.path.join(ROOT, "input_adaptive_block_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    offs = mod.first_mfma_offsets()
+    key = [k for k in offs if "bsattn_bf16_kernelILi128ELb0E" in k]
+    assert len(key) == 1, sorted(offs)
+    assert offs[key[0]] % 32 == 16, offs[key[0]]
